@@ -1,0 +1,18 @@
+"""Plain fp64 CPU oracle for sparse MLA decode over top-k ids.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this package.
+The product path (the HIP library and its Python binding) never imports it and
+shares no code, header, table or helper with it.
+"""
+from .smla_oracle import (  # noqa: F401
+    attention_rows,
+    bf16_to_f64,
+    convert_index,
+    decode_records,
+    e4m3fn_to_f64,
+    flatten_bhs_lse,
+    merge_lse,
+    sparse_mla_decode,
+    transpose_hT_lse,
+)

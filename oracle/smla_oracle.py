@@ -1,0 +1,217 @@
+"""fp64 CPU oracle: sparse MLA decode over indexer top-k ids, fp8_ds_mla cache.
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module.  It shares no code with the HIP path.
+
+What it follows (the three pages this project is built from):
+
+* Page "FlashMLA sparse fp8 path gains DCP and MTP" (prhub.com.cn summary of
+  vLLM pull request 46514), sections "Implementation breakdown" (steps 1-3 and 5)
+  and "Key source snippets" (flashmla_sparse.py ``_forward_fp8_kv_mixed_batch``,
+  flashmla.py ``forward_mqa`` LSE flatten, and the test that neutralises empty
+  rows).
+* Page "[eldritch] attention: support DCP in SM120 FlashInfer sparse MLA"
+  (local-inference-lab/vllm pull request 60), sections "Summary", "Why" and
+  "Scope / Limitations" (global -> local DCP slot conversion, LSE returned for the
+  DCP merge, packed fp8_ds_mla cache).
+* Page "[Bugfix][Attention] Stabilize sparse-MLA DCP for GLM PCP evals"
+  (vllm-project/vllm pull request 55879), "Root causes and fixes", subsection
+  "Zero-local-sequence DCP warmup rank" (a shard with no local rows emits -inf LSE).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* R1 record layout: 656 bytes = 512 e4m3fn codes, 4 fp32 LE scales (scale i for
+  latent dims 128i..128i+127), 64 bf16 LE rope values.  The pages give only the
+  size (656 against 576 for the plain layout), so this order is a choice, and
+  agreement with any real-world fp8_ds_mla byte order is parity unpinned.
+* R2 fp8 flavour: OCP E4M3FN (bias 7, max 448, S.1111.111 is NaN, no infinities).
+* R3 q = [latent 512 | rope 64]; key = [dequantised latent | rope]; value = the
+  dequantised latent only (the output is 512 wide).
+* R4 LSE is the natural log-sum-exp of the scaled logits sm_scale * <q, k>.
+* R5 any negative id is "no candidate"; every remaining list entry is its own term
+  (duplicates count twice); a slot outside [0, num_slots) is skipped like -1.
+* R6 DCP ownership with interleave I: owner = (id // I) % D, local position =
+  (id // (I * D)) * I + id % I; with I = 1 token t lives on shard t % D at t // D.
+* R7 a row with no candidate (all -1, padded row, empty shard) is (out = 0,
+  lse = -inf), the identity of the LSE merge; a merge whose inputs are all -inf
+  is (0, -inf) too, never NaN.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LATENT = 512
+ROPE = 64
+TILE = 128
+RECORD = 656
+
+
+# ----------------------------------------------------------------- element decoders
+
+def e4m3fn_to_f64(codes) -> np.ndarray:
+    """Value of OCP E4M3FN codes (reading R2): sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent field 0 is subnormal (2^-6 * m/8); S.1111.111 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    subnormal = np.ldexp(m / 8.0, -6)
+    v = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 0xF) & (c & 0x7 == 0x7), np.nan, v)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Value of bf16 bit patterns: the upper half of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+_E4M3_TABLE = e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
+
+
+def decode_records(rec) -> tuple:
+    """Dequantise fp8_ds_mla records [n, 656] -> (latent [n,512], rope [n,64]) in fp64.
+
+    latent[d] = e4m3(code[d]) * scale[d // 128] (reading R1); rope is bf16 as stored.
+    Page "[eldritch] attention: support DCP in SM120 FlashInfer sparse MLA",
+    "Scope / Limitations" names the packed fp8_ds_mla layout; the 656-byte size is
+    stated on page "FlashMLA sparse fp8 path gains DCP and MTP", "Related".
+    """
+    rec = np.ascontiguousarray(np.asarray(rec, dtype=np.uint8).reshape(-1, RECORD))
+    n = rec.shape[0]
+    codes = rec[:, :LATENT]
+    scales = rec[:, LATENT:LATENT + 16].copy().view("<f4").astype(np.float64)  # [n,4]
+    rope_bits = rec[:, LATENT + 16:].copy().view("<u2")  # [n,64]
+    latent = _E4M3_TABLE[codes] * np.repeat(scales, TILE, axis=1)
+    return latent.reshape(n, LATENT), bf16_to_f64(rope_bits).reshape(n, ROPE)
+
+
+# ----------------------------------------------------------------- index conversion
+
+def convert_index(ids, req, block_table, block_size, dcp_size=1, dcp_rank=0, interleave=1):
+    """Global top-k token ids -> physical cache slots, -1 where there is no candidate.
+
+    Page "FlashMLA sparse fp8 path gains DCP and MTP", "Implementation breakdown"
+    step 2 and "Key source snippets" (``_forward_fp8_kv_mixed_batch``): without DCP
+    each request-relative id goes through the request's block table; under DCP the
+    ids this rank does not own are set to -1 in place (no front compaction) and the
+    rest become local slots of the rank's shard (reading R6).  ``req`` is the row's
+    request (rows beyond the top-k rows are not used).  Returns (slots [T,K] int32,
+    valid [T] int32 = number of entries that are not -1).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    req = np.asarray(req, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    T, K = ids.shape
+    R, W = bt.shape
+    B, D, r, I = int(block_size), int(dcp_size), int(dcp_rank), int(interleave)
+
+    keep = ids >= 0
+    if D > 1:
+        owner = (ids // I) % D
+        keep &= owner == r
+        pos = (ids // (I * D)) * I + ids % I
+    else:
+        pos = ids.copy()
+    pos = np.where(keep, pos, 0)
+    blk = pos // B
+    rq = np.broadcast_to(req[:, None], (T, K))
+    keep &= (rq >= 0) & (rq < R) & (blk < W)
+    phys = np.full((T, K), -1, dtype=np.int64)
+    phys[keep] = bt[rq[keep], blk[keep]]
+    keep &= phys >= 0
+    slots = np.where(keep, phys * B + pos % B, -1)
+    return slots.astype(np.int32), keep.sum(axis=1).astype(np.int32)
+
+
+# ----------------------------------------------------------------- attention
+
+def _gather(cache, slots):
+    if hasattr(cache, "gather"):
+        return cache.gather(slots)
+    return np.asarray(cache)[np.asarray(slots, dtype=np.int64)]
+
+
+def attention_rows(q, slots, cache, num_slots, sm_scale):
+    """Softmax attention of each (row, head) over the row's own candidate records.
+
+    Page "FlashMLA sparse fp8 path gains DCP and MTP", "Key source snippets": the
+    fp8 kernel is called per query row with that row's top-k slot list and returns
+    the output and the LSE; -1 entries are masked natively.  For a row with slot
+    multiset J (reading R5):  s_j = sm_scale * <q, k_j>,  lse = log sum_j exp(s_j),
+    out = sum_j exp(s_j - lse) * v_j.  A row with no candidate is (0, -inf)
+    (reading R7, same page, "Implementation breakdown" step 3).
+
+    q [T,H,576] float (fp64 arithmetic); slots [T,K]; cache: [num_slots,656] uint8
+    array or an object with ``gather(slots) -> [n,656] bytes``.
+    Returns out [T,H,512] fp64, lse [T,H] fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    slots = np.asarray(slots, dtype=np.int64)
+    T, H, _ = q.shape
+    out = np.zeros((T, H, LATENT), dtype=np.float64)
+    lse = np.full((T, H), -np.inf, dtype=np.float64)
+    for t in range(T):
+        row = slots[t]
+        J = row[(row >= 0) & (row < num_slots)]
+        if J.size == 0:
+            continue
+        latent, rope = decode_records(_gather(cache, J))
+        keys = np.concatenate([latent, rope], axis=1)  # [n,576]
+        s = sm_scale * (q[t] @ keys.T)  # [H,n]
+        m = s.max(axis=1, keepdims=True)
+        l = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+        p = np.exp(s - l[:, None])
+        out[t] = p @ latent
+        lse[t] = l
+    return out, lse
+
+
+def sparse_mla_decode(q, slots, cache, num_slots, sm_scale):
+    """Same as :func:`attention_rows`; named after the library call it checks."""
+    return attention_rows(q, slots, cache, num_slots, sm_scale)
+
+
+# ----------------------------------------------------------------- DCP merge and layouts
+
+def merge_lse(outs, lses):
+    """Combine S shard partials (out_s [S,T,H,Dv], lse_s [S,T,H]) into (out, lse).
+
+    lse = log sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * out_s.  An all -inf
+    entry is (0, -inf): (0, -inf) is the merge identity, so an empty shard changes
+    nothing and never brings in NaN (page "FlashMLA sparse fp8 path gains DCP and
+    MTP", "Implementation breakdown" step 3; page "[eldritch] attention: support DCP
+    in SM120 FlashInfer sparse MLA", "Why": the common MLA layer merges the ranks'
+    partial results with the returned LSE).
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    m = lses.max(axis=0)  # [T,H]
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.exp(lses - m_safe[None])  # exp(-inf) = 0
+    tot = w.sum(axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    wn = w / np.where(finite, tot, 1.0)[None]
+    out = (wn[..., None] * outs).sum(axis=0)
+    out[~finite] = 0.0
+    return out, lse
+
+
+def transpose_hT_lse(lse_1ht):
+    """Kernel-native LSE layout (1, H, T) -> (T, H) for the cross-rank merge
+    (page "FlashMLA sparse fp8 path gains DCP and MTP", "Implementation breakdown"
+    step 1 and the flashmla_sparse.py snippet: squeeze the batch axis, transpose)."""
+    a = np.asarray(lse_1ht)
+    return a.reshape(a.shape[-2], a.shape[-1]).T.copy()
+
+
+def flatten_bhs_lse(lse_bhs):
+    """Dense-decode LSE [batch, heads, seq_len] -> [batch * seq_len, heads], row b*S + s
+    (page "FlashMLA sparse fp8 path gains DCP and MTP", "Implementation breakdown"
+    step 5 and the flashmla.py snippet: permute(0, 2, 1) then reshape)."""
+    a = np.asarray(lse_bhs)
+    Bn, H, S = a.shape
+    return np.transpose(a, (0, 2, 1)).reshape(Bn * S, H).copy()
