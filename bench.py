@@ -1,0 +1,205 @@
+"""Throughput of the sparse-MLA decode step on one MI355X.
+
+Workload: MTP / speculative decode batch, 64 requests x 4 query tokens (T = 256 rows),
+H = 128 heads, context 32768 per request, top-k 2048 causal ids per row, fp8_ds_mla cache,
+simulated DCP2 (two shard caches on the same GPU).  One step = for each shard, index
+conversion + decode (fp32 partial out, LSE in the kernel-native (H, T) layout), then the
+LSE merge into bf16 out and (T, H) LSE.
+
+Prints one JSON line on stdout.  `value` is query rows per second of the whole step with
+every input resident in HBM.  `roofline` covers the decode kernel: algorithmic bytes and
+flops per launch over its mean launch time (HIP events on the launch stream).
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode query-rows/s and KV GB/s (H=128, topk=2048) + % roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FLOP_PER_VALID_ID_PER_HEAD = 2 * (576 + 512)  # QK^T over 576 dims + PV over 512 dims
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_algorithmic(T, H, K, nvalid, out_bytes):
+    """Bytes and flops one decode launch must move / compute."""
+    byts = 656 * nvalid + T * H * 576 * 2 + T * K * 4 + T * H * (512 * out_bytes + 4)
+    flops = FLOP_PER_VALID_ID_PER_HEAD * H * nvalid
+    return byts, flops
+
+
+def roofline_entry(byts, flops, seconds):
+    t_hbm = byts / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = byts / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+
+
+def cpu_baseline(w, budget_s):
+    """fp64 oracle of the same DCP2 step (converts, shard attention, merge) on the first rows
+    until the time budget is spent; rows/s over the rows done."""
+    import numpy as np
+    import oracle.smla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rows_done, t0 = 0, time.perf_counter()
+    chunk = 4
+    while rows_done < w.T and time.perf_counter() - t0 < budget_s:
+        rows = list(range(rows_done, min(w.T, rows_done + chunk)))
+        sub = w.rows(rows)
+        q = sub.q_f32()
+        outs, lses = [], []
+        for sh in sub.shards:
+            s, _ = O.convert_index(sub.ids, sub.req, sh.block_table, sub.block_size, sub.dcp_size, sh.rank)
+            o, l = O.attention_rows(q, s, sh.cache, sh.cache.num_slots, sub.sm_scale)
+            outs.append(o)
+            lses.append(l)
+        O.merge_lse(np.stack(outs), np.stack(lses))
+        rows_done += len(rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(rows_done / dt, 3), "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows_done} of {w.T} rows of the same DCP2 step (fp64 numpy oracle: 2 shard converts, "
+                      f"shard attention, LSE merge), {dt:.1f} s on {os.cpu_count()} host CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=2, help="cache copies rotated between steps (beat the 256 MB MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
+              f"the DCP shards are simulated on one device", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_mla_decode_topk_amd as smla
+    from sparse_mla_decode_topk_amd.pipeline import DcpDecodeStep, device_shards
+    from workload import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    smla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    log("generating workload c3 (T=256, H=128, top-k 2048, ctx 32768, DCP2) ...")
+    t0 = time.perf_counter()
+    w = make_config(3)
+    log(f"  generated in {time.perf_counter() - t0:.1f} s; copying caches to the GPU ({args.replicas} replicas)")
+    q = w.q_torch().to(dev)
+    ids = torch.from_numpy(w.ids).to(dev)
+    req = torch.from_numpy(w.req).to(dev)
+    replicas = [device_shards(w, dev) for _ in range(max(1, args.replicas))]
+    unsharded_cache = w.cache.to_device(dev)
+    unsharded_bt = torch.from_numpy(w.block_table).to(dev)
+    torch.cuda.synchronize()
+
+    step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=w.dcp_size, block_size=w.block_size,
+                         softmax_scale=w.sm_scale, out_dtype=torch.bfloat16, partial_dtype=torch.float32,
+                         lse_layout="HT", device=dev)
+    # valid ids per shard (host-side count from the inputs, outside any timed region)
+    nvalid = [int((np.asarray(w.ids) >= 0).sum())]
+    shard_valid = []
+    for r in range(w.dcp_size):
+        own = (w.ids >= 0) & ((w.ids % w.dcp_size) == r)
+        shard_valid.append(int(own.sum()))
+
+    decode_events = []  # (start, end) events around every decode launch, on the launch stream
+    stream = torch.cuda.current_stream(dev)
+
+    def run_step(i, events=None):
+        return step.run(q, ids, req, replicas[i % len(replicas)], decode_events=events)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run_step(i, decode_events)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    dec_ms = [a.elapsed_time(b) for a, b in decode_events]
+    ms_per_step = wall * 1e3 / args.steps
+    rows_per_s = w.T * args.steps / wall
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {gpu_ms / args.steps:.4f} ms/step events")
+
+    # decode kernel roofline: mean over the timed launches (both shards have ~the same valid count)
+    mean_dec_s = float(np.mean(dec_ms)) / 1e3
+    nv_mean = float(np.mean(shard_valid))
+    byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, out_bytes=4)
+    roof = roofline_entry(byts, flops, mean_dec_s)
+    roof["traffic"] = None
+    roof["kernel"] = "decode_kernel<2> (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
+    roof["launch_us"] = round(mean_dec_s * 1e6, 2)
+    roof["algorithmic_bytes"] = int(byts)
+    roof["algorithmic_flops"] = int(flops)
+    kv_gbps = 656 * sum(shard_valid) * args.steps / (float(np.sum(dec_ms)) / 1e3) / 1e9
+
+    # the unsharded H=128 / top-k 2048 decode of the same rows (reported beside the step)
+    one = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=1, block_size=w.block_size, softmax_scale=w.sm_scale,
+                        out_dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        one.run(q, ids, req, [(unsharded_cache, unsharded_bt)])
+    torch.cuda.synchronize()
+    decode_events.clear()
+    for _ in range(max(10, args.steps // 2)):
+        one.run(q, ids, req, [(unsharded_cache, unsharded_bt)], decode_events=decode_events)
+    torch.cuda.synchronize()
+    un_s = float(np.mean([a.elapsed_time(b) for a, b in decode_events])) / 1e3
+    ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], out_bytes=2)
+    unsharded = {"decode_us": round(un_s * 1e6, 2), "tflops": round(uf / un_s / 1e12, 1),
+                 "kv_gbps": round(656 * nvalid[0] / un_s / 1e9, 1), "roofline": roofline_entry(ub, uf, un_s)}
+
+    line = {
+        "metric": METRIC, "value": round(rows_per_s, 1), "unit": "query-rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "c3_mtp_dcp2: 64 req x 4 MTP tokens (T=256), H=128, top-k 2048 causal, ctx 32768, "
+                               "fp8_ds_mla cache, simulated DCP2 (convert+decode per shard, LSE merge)",
+                   "T": w.T, "H": w.H, "topk": w.K, "ctx": 32768, "dcp": w.dcp_size, "block_size": w.block_size,
+                   "cache_replicas": len(replicas)},
+        "kv_gbps": round(kv_gbps, 1),
+        "roofline": roof,
+        "unsharded_decode": unsharded,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

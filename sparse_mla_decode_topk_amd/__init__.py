@@ -1,0 +1,24 @@
+"""Sparse MLA decode over indexer top-k ids against a packed fp8_ds_mla cache, MI355X.
+
+The compute lives in libsmla.so (hand-written HIP for gfx950, C ABI in include/smla.h);
+this package is a thin ctypes binding with the same call names that marshals torch
+tensors (device memory and streams only) into the C calls.
+"""
+from ._binding import (  # noqa: F401
+    HEAD_DIM,
+    LATENT_DIM,
+    RECORD_BYTES,
+    SmlaError,
+    abi_version,
+    convert_index,
+    decode,
+    decode_workspace_size,
+    lib_path,
+    load_library,
+    merge_lse,
+    sparse_mla_convert_index,
+    sparse_mla_decode,
+    sparse_mla_decode_workspace_size,
+    sparse_mla_merge_lse,
+    workspace_for,
+)

@@ -1,0 +1,249 @@
+"""ctypes binding of libsmla.so: argument marshalling only.
+
+Every function here checks dtypes, devices and layouts of torch tensors, passes raw
+device pointers, strides and the current HIP stream to the C call of the same name, and
+raises SmlaError on a non-zero status.  All arithmetic happens in the HIP kernels; there
+is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+LATENT_DIM = 512
+ROPE_DIM = 64
+HEAD_DIM = LATENT_DIM + ROPE_DIM
+RECORD_BYTES = 656
+
+_BF16, _FP32 = 0, 1
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: status {status}: {text}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.environ.get("SMLA_LIB", os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmla.so"))
+
+
+def load_library():
+    """Load libsmla.so once and declare the C signatures (include/smla.h)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(path)
+        lib.smla_abi_version.restype = ctypes.c_int
+        lib.smla_abi_version.argtypes = []
+        lib.smla_status_string.restype = ctypes.c_char_p
+        lib.smla_status_string.argtypes = [ctypes.c_int]
+        lib.sparse_mla_convert_index.restype = ctypes.c_int
+        lib.sparse_mla_convert_index.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                 _P, _I64, _P, _P]
+        lib.sparse_mla_decode_workspace_size.restype = _SZ
+        lib.sparse_mla_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
+        lib.sparse_mla_decode.restype = ctypes.c_int
+        lib.sparse_mla_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _F32, _P, _I32, _I64,
+                                          _I64, _P, _I64, _I64, _I32, _P, _SZ, _P]
+        lib.sparse_mla_merge_lse.restype = ctypes.c_int
+        lib.sparse_mla_merge_lse.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I32,
+                                             _I64, _I64, _P, _I64, _I64, _P]
+        _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return load_library().smla_abi_version()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SmlaError(fn, status, load_library().smla_status_string(status).decode())
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _BF16
+    if dtype == torch.float32:
+        return _FP32
+    raise TypeError(f"unsupported dtype {dtype}: bfloat16 or float32")
+
+
+# ------------------------------------------------------------------ raw C-named calls
+
+def sparse_mla_convert_index(*args) -> int:
+    return load_library().sparse_mla_convert_index(*args)
+
+
+def sparse_mla_decode_workspace_size(T: int, H: int, K: int, num_splits: int = 0) -> int:
+    return int(load_library().sparse_mla_decode_workspace_size(T, H, K, num_splits))
+
+
+def sparse_mla_decode(*args) -> int:
+    return load_library().sparse_mla_decode(*args)
+
+
+def sparse_mla_merge_lse(*args) -> int:
+    return load_library().sparse_mla_merge_lse(*args)
+
+
+decode_workspace_size = sparse_mla_decode_workspace_size
+
+# ------------------------------------------------------------------ tensor-level calls
+
+_ws_cache = {}
+
+
+def workspace_for(T: int, H: int, K: int, device, num_splits: int = 0) -> Optional[torch.Tensor]:
+    """A per-device workspace at least as large as the call needs (cached and grown outside the
+    hot path; the library itself never allocates)."""
+    need = sparse_mla_decode_workspace_size(T, H, K, num_splits)
+    if need == 0:
+        return None
+    device = torch.device(device)
+    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def convert_index(topk_ids: torch.Tensor, req_id_per_token: torch.Tensor, block_table: torch.Tensor,
+                  block_size: int, dcp_size: int = 1, dcp_rank: int = 0, interleave: int = 1,
+                  out: Optional[torch.Tensor] = None, with_valid_count: bool = True
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Global top-k ids [T,K] -> slots [T,K] (and per-row valid counts [T])."""
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(req_id_per_token, "req_id_per_token", torch.int32, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    T, K = topk_ids.shape
+    if (K > 1 and topk_ids.stride(1) != 1) or (block_table.shape[1] > 1 and block_table.stride(1) != 1) or \
+            (req_id_per_token.shape[0] > 1 and req_id_per_token.stride(0) != 1):
+        raise ValueError("index arrays need a contiguous last dimension")
+    if req_id_per_token.shape[0] < T:
+        raise ValueError("req_id_per_token must cover every top-k row")
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=topk_ids.device)
+    _need(out, "out", torch.int32, 2)
+    if tuple(out.shape) != (T, K) or (K > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [T,K] with a contiguous last dimension")
+    valid = torch.empty((T,), dtype=torch.int32, device=topk_ids.device) if with_valid_count else None
+    R, W = block_table.shape
+    st = sparse_mla_convert_index(
+        topk_ids.data_ptr(), topk_ids.stride(0), req_id_per_token.data_ptr(), block_table.data_ptr(),
+        block_table.stride(0), R, W, T, K, block_size, dcp_size, dcp_rank, interleave, out.data_ptr(), out.stride(0),
+        valid.data_ptr() if valid is not None else None, _stream(topk_ids.device))
+    _check("sparse_mla_convert_index", st)
+    return out, valid
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax_scale: float,
+           out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+           lse: Optional[torch.Tensor] = None, lse_layout: str = "TH", num_splits: int = 0,
+           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse MLA decode.  q [T,H,576] bf16, kv_cache [num_slots,656] uint8, slots [T,K] int32.
+
+    Returns out [T,H,512] (out_dtype) and lse.  lse_layout "TH" gives a [T,H] tensor;
+    "HT" writes the kernel-native [H,T] layout and returns its [T,H] transposed view.
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_cache, "kv_cache", torch.uint8, 2)
+    _need(slots, "slots", torch.int32, 2)
+    T, H, D = q.shape
+    if D != HEAD_DIM or q.stride(2) != 1:
+        raise ValueError("q must be [T,H,576] with contiguous dims")
+    if kv_cache.shape[1] != RECORD_BYTES or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_slots,656] uint8 tensor")
+    K = slots.shape[1]
+    if slots.shape[0] != T or (K > 1 and slots.stride(1) != 1):
+        raise ValueError("slots must be [T,K] with a contiguous last dimension")
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=out_dtype, device=dev)
+    _need(out, "out", out.dtype, 3)
+    if tuple(out.shape) != (T, H, LATENT_DIM) or out.stride(2) != 1:
+        raise ValueError("out must be [T,H,512] with contiguous dims")
+    if lse is None:
+        if lse_layout == "TH":
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        elif lse_layout == "HT":
+            lse = torch.empty((H, T), dtype=torch.float32, device=dev).t()
+        else:
+            raise ValueError("lse_layout must be 'TH' or 'HT'")
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(lse.shape) != (T, H):
+        raise ValueError("lse must be viewable as [T,H]")
+    if workspace is None:
+        workspace = workspace_for(T, H, K, dev, num_splits)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None \
+        else (None, 0)
+    if ws_ptr is not None and ws_ptr % 256:
+        pad = (-ws_ptr) % 256
+        ws_ptr, ws_bytes = ws_ptr + pad, ws_bytes - pad
+    st = sparse_mla_decode(
+        q.data_ptr(), q.stride(0), q.stride(1), kv_cache.data_ptr(), kv_cache.shape[0], slots.data_ptr(),
+        slots.stride(0), T, H, K, float(softmax_scale), out.data_ptr(), _dtype_code(out.dtype), out.stride(0),
+        out.stride(1), lse.data_ptr(), lse.stride(0), lse.stride(1), num_splits, ws_ptr, ws_bytes, _stream(dev))
+    _check("sparse_mla_decode", st)
+    return out, lse
+
+
+def merge_lse(out_parts: torch.Tensor, lse_parts: torch.Tensor, out: Optional[torch.Tensor] = None,
+              out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge S partials: out_parts [S,T,H,512], lse_parts [S,T,H] (any strides)."""
+    _need(out_parts, "out_parts", out_parts.dtype, 4)
+    _need(lse_parts, "lse_parts", torch.float32, 3)
+    S, T, H, D = out_parts.shape
+    if D != LATENT_DIM or out_parts.stride(3) != 1:
+        raise ValueError("out_parts must be [S,T,H,512] with contiguous dims")
+    if tuple(lse_parts.shape) != (S, T, H):
+        raise ValueError("lse_parts must be [S,T,H]")
+    dev = out_parts.device
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=out_dtype or out_parts.dtype, device=dev)
+    if tuple(out.shape) != (T, H, LATENT_DIM) or out.stride(2) != 1:
+        raise ValueError("out must be [T,H,512] with contiguous dims")
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(lse, "lse", torch.float32, 2)
+    st = sparse_mla_merge_lse(
+        out_parts.data_ptr(), _dtype_code(out_parts.dtype), out_parts.stride(0), out_parts.stride(1),
+        out_parts.stride(2), lse_parts.data_ptr(), lse_parts.stride(0), lse_parts.stride(1), lse_parts.stride(2),
+        S, T, H, out.data_ptr(), _dtype_code(out.dtype), out.stride(0), out.stride(1), lse.data_ptr(), lse.stride(0),
+        lse.stride(1), _stream(dev))
+    _check("sparse_mla_merge_lse", st)
+    return out, lse

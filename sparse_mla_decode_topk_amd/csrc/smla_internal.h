@@ -1,0 +1,78 @@
+// Internal declarations shared by the HIP sources of libsmla (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kHeadDim = kLatent + kRope;  // 576
+constexpr int kRecordBytes = 656;          // 512 e4m3 codes + 4 fp32 scales + 64 bf16 rope
+constexpr int kScaleOffset = 512;
+constexpr int kRopeOffset = 528;
+constexpr int kMaxEntriesPerSplit = 2048;  // slot entries one decode workgroup compacts
+constexpr int kMaxSplits = 64;
+constexpr int kHeadsPerWave = 32;
+
+struct ConvertParams {
+  const int32_t* ids;
+  int64_t ids_ld;
+  const int32_t* req;
+  const int32_t* bt;
+  int64_t bt_ld;
+  int32_t bt_rows, bt_width;
+  int32_t T, K, block_size, dcp_size, dcp_rank, interleave;
+  int32_t* slots;
+  int64_t slots_ld;
+  int32_t* valid;
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  const uint8_t* kv;
+  int64_t num_slots;
+  const int32_t* slots;
+  int64_t slots_ld;
+  int32_t T, H, K;
+  float scale_log2;  // softmax_scale * log2(e)
+  void* out;
+  int32_t out_fp32;
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t l_st, l_sh;
+  int32_t splits, entries_per_split, head_blocks, heads_per_block;
+  float* ws_o;    // [T, splits, H, 512] unnormalised partial outputs
+  float* ws_ml;   // [T, splits, H, 2]   (running max in log2 units, sum)
+  int32_t* ws_cnt;  // [T, head_blocks] arrival counters, left at zero
+};
+
+struct MergeParams {
+  const void* parts;
+  int32_t part_fp32;
+  int64_t p_ss, p_st, p_sh;
+  const float* lparts;
+  int64_t lp_ss, lp_st, lp_sh;
+  int32_t S, T, H;
+  void* out;
+  int32_t out_fp32;
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t l_st, l_sh;
+};
+
+struct DecodePlan {
+  int32_t waves;        // waves per workgroup (32 heads each)
+  int32_t head_blocks;  // workgroups per row along heads
+  int32_t splits;       // top-k ranges per row
+  int32_t entries_per_split;
+  size_t ws_o_bytes, ws_ml_bytes, ws_cnt_bytes, ws_total;
+};
+
+hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,136 @@
+"""Sparse MLA decode on the GPU against the fp64 oracle (max |dout| <= 2e-2, max |dlse| <= 1e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.smla_oracle as O
+import sparse_mla_decode_topk_amd as smla
+from tests.gpu_common import check_close, dev, oracle_unsharded, q_dev, require_gpu
+from workload import make_config, make_random
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gpu_decode(w, slots_np=None, out_dtype=None, num_splits=0, lse_layout="TH", cache=None):
+    if slots_np is None:
+        slots_np, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    cache = w.cache.to_device("cuda") if cache is None else cache
+    od = out_dtype or (torch.float32 if w.out_dtype == "fp32" else torch.bfloat16)
+    out, lse = smla.decode(q_dev(w), cache, dev(slots_np), w.sm_scale, out_dtype=od, num_splits=num_splits,
+                           lse_layout=lse_layout)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("cid", [0, 1])
+def test_decode_config(cid):
+    w = make_config(cid)
+    print(f"decode config {cid}: T={w.T} H={w.H} K={w.K}", flush=True)
+    out, lse = gpu_decode(w)
+    ref_o, ref_l = oracle_unsharded(w)
+    do, dl = check_close(out, lse, ref_o, ref_l, what=w.name)
+    print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 96, 128])
+@pytest.mark.parametrize("K,neg", [(1, 0.0), (7, 0.0), (64, 0.3), (100, 0.5), (2048, 0.1)])
+def test_decode_random_shapes(H, K, neg):
+    w = make_random(1000 + H + K, T=5, H=H, K=K, ctx=max(2 * K, 64), B=64, neg_frac=neg, n_req=2)
+    print(f"decode random H={H} K={K} neg={neg}", flush=True)
+    out, lse = gpu_decode(w, out_dtype=torch.float32)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what=f"H{H}K{K}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_forced_splits(splits, dtype):
+    w = make_random(2000 + splits, T=6, H=64, K=700, ctx=1500, B=64, neg_frac=0.2, n_req=3)
+    print(f"decode splits={splits} dtype={dtype}", flush=True)
+    out, lse = gpu_decode(w, out_dtype=dtype, num_splits=splits)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what=f"splits{splits}")
+
+
+def test_decode_split_ranges_with_empty_splits():
+    # valid entries only in the first quarter: later splits see nothing and must drop out
+    w = make_random(31, T=4, H=128, K=1024, ctx=4096, B=64, n_req=2)
+    w.ids[:, 256:] = -1
+    out, lse = gpu_decode(w, out_dtype=torch.float32, num_splits=4)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what="empty splits")
+
+
+def test_decode_empty_rows_and_out_of_range_slots():
+    w = make_random(41, T=6, H=64, K=64, ctx=200, B=16, n_req=2)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    slots[1, :] = -1  # empty row
+    slots[2, :] = w.cache.num_slots + 5  # only out-of-range entries: empty too
+    slots[3, ::2] = -7  # other negatives
+    slots[4, 3] = w.cache.num_slots  # one out-of-range entry among valid ones
+    for splits in (1, 3):
+        out, lse = gpu_decode(w, slots_np=slots, out_dtype=torch.float32, num_splits=splits)
+        ref_o, ref_l = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale)
+        check_close(out, lse, ref_o, ref_l, what=f"empty rows s{splits}")
+        l = lse.cpu().numpy()
+        assert np.all(np.isneginf(l[1])) and np.all(np.isneginf(l[2]))
+        assert torch.all(out[1] == 0) and torch.all(out[2] == 0)
+
+
+def test_decode_k_zero_and_t_zero():
+    w = make_random(51, T=3, H=32, K=4, ctx=40, B=16)
+    slots = np.zeros((3, 0), dtype=np.int32)
+    out, lse = gpu_decode(w, slots_np=slots)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    q = torch.zeros((0, 32, 576), dtype=torch.bfloat16, device="cuda")
+    o, l = smla.decode(q, w.cache.to_device("cuda"), torch.zeros((0, 4), dtype=torch.int32, device="cuda"), 0.1)
+    assert o.shape == (0, 32, 512)
+
+
+def test_decode_duplicates_count_twice():
+    w = make_random(61, T=3, H=16, K=12, ctx=60, B=16)
+    w.ids[0, 1] = w.ids[0, 0]
+    w.ids[1, :] = w.ids[1, 0]
+    out, lse = gpu_decode(w, out_dtype=torch.float32)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what="duplicates")
+
+
+def test_lse_layouts_agree_bitwise():
+    w = make_random(71, T=9, H=128, K=256, ctx=1024, B=64, neg_frac=0.2, n_req=3)
+    cache = w.cache.to_device("cuda")
+    o1, l1 = gpu_decode(w, lse_layout="TH", cache=cache)
+    o2, l2 = gpu_decode(w, lse_layout="HT", cache=cache)
+    assert l2.stride() == (1, 9)
+    assert torch.equal(l1, l2) and torch.equal(o1, o2)
+    # the (1, H, T) -> (T, H) transpose of the native layout matches the oracle's reading
+    native = l2.t().contiguous().cpu().numpy()[None]
+    assert np.array_equal(O.transpose_hT_lse(native), l1.cpu().numpy())
+
+
+def test_decode_strided_q_and_out():
+    w = make_random(81, T=4, H=64, K=128, ctx=512, B=64)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    qbig = torch.zeros((4, 80, 576 + 64), dtype=torch.bfloat16, device="cuda")
+    qv = qbig[:, 8:72, :576]
+    qv.copy_(q_dev(w))
+    obig = torch.full((4, 70, 520), 7.0, dtype=torch.float32, device="cuda")
+    ov = obig[:, 3:67, :512]
+    out, lse = smla.decode(qv, w.cache.to_device("cuda"), dev(slots), w.sm_scale, out=ov)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(ov, lse, ref_o, ref_l, what="strided")
+    assert torch.all(obig[:, :3] == 7.0) and torch.all(obig[:, :, 512:] == 7.0)
+
+
+def test_decode_repeat_is_deterministic():
+    w = make_random(91, T=8, H=128, K=512, ctx=2048, B=64, n_req=2)
+    cache = w.cache.to_device("cuda")
+    a = gpu_decode(w, cache=cache, num_splits=4)
+    b = gpu_decode(w, cache=cache, num_splits=4)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -1,0 +1,147 @@
+"""Simulated-DCP pipelines (convert -> decode per shard -> LSE merge) and the merge kernel on
+the GPU against the oracle, at the configurations' real sizes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.smla_oracle as O
+import sparse_mla_decode_topk_amd as smla
+from sparse_mla_decode_topk_amd.pipeline import DcpDecodeStep, device_shards
+from tests.gpu_common import check_close, dev, oracle_unsharded, q_dev, require_gpu
+from workload import make_config, make_random
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def out_dtype_of(w):
+    return torch.float32 if w.out_dtype == "fp32" else torch.bfloat16
+
+
+def run_step(w, shards=None, **kw):
+    shards = shards or device_shards(w)
+    step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=w.dcp_size, block_size=w.block_size,
+                         softmax_scale=w.sm_scale, out_dtype=out_dtype_of(w), **kw)
+    out, lse = step.run(q_dev(w), dev(w.ids), dev(w.req), shards)
+    torch.cuda.synchronize()
+    return step, out, lse
+
+
+def unsharded_gpu(w):
+    step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=1, block_size=w.block_size, softmax_scale=w.sm_scale,
+                         out_dtype=out_dtype_of(w))
+    out, lse = step.run(q_dev(w), dev(w.ids), dev(w.req),
+                        [(w.cache.to_device("cuda"), dev(w.block_table))])
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_dcp4_c2_full():
+    w = make_config(2)
+    print(f"c2: T={w.T} H={w.H} D={w.dcp_size}", flush=True)
+    step, out, lse = run_step(w)
+    ref_o, ref_l = oracle_unsharded(w)
+    do, dl = check_close(out, lse, ref_o, ref_l, what="c2 merged vs oracle")
+    print(f"  merged vs oracle max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+    # the four context-2 rows: shards 2 and 3 own no candidate and emit (0, -inf)
+    lp = step.lse_parts.cpu().numpy()
+    pp = step.parts.float().cpu().numpy()
+    for r in (2, 3):
+        assert np.all(np.isneginf(lp[r, 32:])) and np.all(pp[r, 32:] == 0)
+    for r in (0, 1):
+        assert np.all(np.isfinite(lp[r, 32:]))
+    # merged == unsharded GPU result within the same bar
+    uo, ul = unsharded_gpu(w)
+    check_close(out, lse, uo.float().cpu().numpy().astype(np.float64), ul.cpu().numpy().astype(np.float64),
+                what="c2 merged vs unsharded gpu")
+
+
+def test_dcp2_c3_full_size_sampled():
+    """The timed configuration: MTP rows, H=128, top-k 2048, DCP2, kernel-native (H,T) LSE."""
+    w = make_config(3)
+    print(f"c3: T={w.T} H={w.H} K={w.K}", flush=True)
+    step, out, lse = run_step(w, lse_layout="HT")
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    rows = list(range(0, w.T, 17)) + [w.T - 1]
+    ref_o, ref_l = oracle_unsharded(w, rows)
+    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, what="c3 sampled rows")
+    print(f"  sampled rows max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+    uo, ul = unsharded_gpu(w)
+    check_close(out, lse, uo.float().cpu().numpy().astype(np.float64), ul.cpu().numpy().astype(np.float64),
+                what="c3 merged vs unsharded gpu")
+    ref_o, ref_l = oracle_unsharded(w, rows)
+    check_close(uo[rows], ul[rows], ref_o, ref_l, what="c3 unsharded sampled rows")
+
+
+def test_dcp8_c4_subset_rows_full_caches():
+    """Mixed batch at full context (131072-token decode requests, 8 shards) on a row subset."""
+    w = make_config(4, scale_rows=48)
+    print(f"c4 subset: T={w.T} H={w.H} D={w.dcp_size}", flush=True)
+    step, out, lse = run_step(w, lse_layout="HT")
+    ref_o, ref_l = oracle_unsharded(w)
+    do, dl = check_close(out, lse, ref_o, ref_l, what="c4 subset")
+    print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("S,dtype", [(1, torch.float32), (2, torch.float32), (4, torch.bfloat16), (8, torch.float32)])
+def test_merge_against_oracle(S, dtype):
+    rng = np.random.default_rng(S)
+    T, H = 7, 48
+    parts = rng.standard_normal((S, T, H, 512)).astype(np.float32)
+    lses = (rng.standard_normal((S, T, H)) * 4).astype(np.float32)
+    lses[rng.random((S, T, H)) < 0.3] = -np.inf  # empty partials
+    lses[:, 2, :] = -np.inf  # an entry empty everywhere
+    parts[np.isneginf(lses)] = 0.0  # an empty partial carries out = 0
+    pt = dev(parts).to(dtype)
+    ref_o, ref_l = O.merge_lse(pt.float().cpu().numpy().astype(np.float64), lses.astype(np.float64))
+    out, lse = smla.merge_lse(pt, dev(lses), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_close(out, lse, ref_o, ref_l, out_tol=1e-5, lse_tol=1e-5, what=f"merge S{S}")
+    assert torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
+
+
+def test_merge_identity_is_exact():
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((1, 5, 16, 512)).astype(np.float32)
+    l = rng.standard_normal((1, 5, 16)).astype(np.float32)
+    parts = np.concatenate([o, np.zeros_like(o)])
+    lses = np.concatenate([l, np.full_like(l, -np.inf)])
+    out, lse = smla.merge_lse(dev(parts), dev(lses), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.allclose(out.cpu().numpy(), o[0], rtol=0, atol=2e-6)
+    assert np.allclose(lse.cpu().numpy(), l[0], rtol=0, atol=2e-6)
+
+
+def test_graph_capture_replays_match_eager():
+    w = make_random(401, T=12, H=128, K=512, ctx=2048, B=64, D=2, neg_frac=0.1, n_req=3)
+    shards = device_shards(w)
+    q, ids, req = q_dev(w), dev(w.ids), dev(w.req)
+    for num_splits in (1, 3):  # 3 exercises the workspace and the counter-zeroing kernel
+        step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=2, block_size=w.block_size, softmax_scale=w.sm_scale,
+                             num_splits=num_splits)
+        out, lse = step.run(q, ids, req, shards)
+        torch.cuda.synchronize()
+        eager_o, eager_l = out.clone(), lse.clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step.run(q, ids, req, shards)  # warm up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.run(q, ids, req, shards)
+        for rep in range(3):
+            step.out.fill_(123.0)
+            step.lse.fill_(-5.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(step.out, eager_o), f"replay {rep} splits {num_splits}: out differs"
+            assert torch.equal(step.lse, eager_l), f"replay {rep} splits {num_splits}: lse differs"
+        ref_o, ref_l = oracle_unsharded(w)
+        check_close(step.out, step.lse, ref_o, ref_l, what=f"graph splits{num_splits}")
