@@ -6,29 +6,34 @@
 // "[eldritch] attention: support DCP in SM120 FlashInfer sparse MLA", "Why").
 //
 // gfx950 design
-//  * A workgroup owns one row, up to 64 heads and one range of the row's top-k list.  It
-//    has one wave per SIMD.  Waves come in pairs; a pair owns 32 heads.  Wave half p of a
-//    pair computes the partial scores over latent dims 256p..256p+255 and rope dims
-//    32p..32p+31, the two halves swap partial scores through LDS, and wave p then
-//    accumulates output dims 256p..256p+255.  Per wave that keeps 72 registers of query
-//    and 128 accumulator registers, while every LDS operand byte still feeds 32 heads.
+//  * A workgroup owns one row, up to 128 heads (NW waves x 32) and one range of the row's
+//    top-k list, with one wave per SIMD.  Every gathered record feeds all heads of the row.
+//  * Work split inside the workgroup: wave w computes scores, softmax and probabilities for
+//    its 32 heads over all 576 dims; the probabilities go to LDS; wave w then accumulates
+//    output dims [w*512/NW, (w+1)*512/NW) for ALL heads of the workgroup.  No softmax is
+//    duplicated and every value operand is widened by exactly one wave.
 //  * Gather: the row's slot range is compacted in LDS (-1 and out-of-range entries are
-//    skipped in place of a front-pack on the host), then tiles of 64 records are copied
-//    HBM -> LDS with global_load_lds_dwordx4 (no register staging), double-buffered so the
-//    next tile is in flight while the current one is computed.  Lane r of a load carries
-//    record r of the tile and load j moves 16-byte chunk j of every record, so the tile
-//    sits in LDS chunk-major ([41 chunks][64 records][16 B]): one base address per lane,
-//    and every MFMA operand read below is a contiguous LDS access.
-//  * QK^T: S^T[token, head] = K[token, :] . Q^T on v_mfma_f32_32x32x16_bf16.  The fp8
-//    codes are widened to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1), so the
-//    products are exact; each 128-dim fp32 scale multiplies the fp32 partial dot product
-//    of its tile, and the bf16 rope dims are added unscaled.
-//  * Online softmax in base 2 with a lazy reference max: the accumulators are rescaled
-//    only when the running max grows by more than 8 (probabilities stay <= 2^8).  The
-//    S^T layout puts one head per lane, so row reductions are in-lane plus one swap.
-//  * PV: O^T[dim, head] += V^T[dim, token] . P'^T[token, head] on the same MFMA, with
-//    P' = p * scale(token, tile) rounded once to bf16; V^T fragments come straight from
-//    the tile with ds_read_b64_tr_b8 and are widened to bf16 exactly.
+//    skipped; no front-pack on the host), then tiles of TT records are copied HBM -> LDS
+//    with global_load_lds_dwordx4 (no register staging), double-buffered.  Lane r of a load
+//    carries record r of the tile and load j moves 16-byte chunk j of every record, so the
+//    tile sits in LDS chunk-major ([41 chunks][TT records][16 B]): one base address per
+//    lane, and every MFMA operand read below is a contiguous LDS access.
+//  * QK^T latent part on fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales): the raw
+//    e4m3 codes are the A operand as stored, and q is split exactly into two e4m3 terms,
+//    q * 2^e_h = hi + lo (hi = rne(q * 2^e_h), lo = rne(q * 2^e_h - hi), e_h a per-head power
+//    of two putting max|q| just under 448), so two fp8 MFMAs give the bf16-exact product at
+//    the cost of one bf16 MFMA and no operand widening.  Each 128-dim fp32 record scale
+//    multiplies the fp32 partial dot product of its tile.  Rope dims (bf16) run on
+//    v_mfma_f32_32x32x16_bf16.  S^T (tokens x heads) puts one head per lane, so softmax row
+//    reductions are in-lane plus one cross-half swap.
+//  * Softmax in base 2 against a per-head reference max fixed at the first tile: later
+//    probabilities are 2^(s - ref) and may exceed 1, which fp32 accumulators and bf16
+//    probabilities hold without loss.  Should a score ever exceed the reference by more
+//    than 2^64 the workgroup recomputes the row once with the exact max as reference, so
+//    the accumulators are never rescaled inside the loop.
+//  * PV: O^T[dim, head] += V^T[dim, token] . P'^T[token, head] on bf16 MFMA with
+//    P' = p * scale(token, tile) rounded once to bf16 (written to LDS per scale tile); V^T
+//    fragments come from the tile through ds_read_b64_tr_b8 and are widened exactly.
 //  * Split-K over the top-k list with an in-kernel combine: every split writes its
 //    unnormalised partial (O, max, sum) to the workspace; the last split to arrive (device
 //    scope counter, zeroed by a small kernel before the decode kernel) merges them.
@@ -46,14 +51,15 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 #define SMLA_LDS __attribute__((address_space(3)))
 
-constexpr int TT = 64;       // records per gathered tile
-constexpr int CS = 16 * TT;  // bytes per chunk row of a tile
-constexpr int kStageBytes = 41 * CS;
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr float kRefHeadroom = 64.0f;  // log2 units a score may exceed the reference by
+constexpr int kUnitScale = 127;       // E8M0 encoding of 2^0 for the scaled fp8 MFMA
 
 __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -65,142 +71,57 @@ __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Per-lane state of one wave: 32 heads, its 256 output dims.
-struct WaveState {
-  f32x16 o[8];  // O^T block mb: dims 256*half + 32*mb + 8*(r/4) + 4*(lane/32) + r%4
-  float m_run;  // reference max (log2 units); identical in both waves of a pair
-  float l_run;  // this lane's share of the softmax sum (its 16 tokens of each block)
-};
-
-// One 32-token block: partial QK^T, score swap with the partner wave, softmax update, PV.
-__device__ __forceinline__ void block_compute(const uint8_t* __restrict__ tile, const float* __restrict__ sct,
-                                              float* __restrict__ xs_mine, const float* __restrict__ xs_peer,
-                                              int blk, int nvalid, const bf16x8 (&qr)[18], WaveState& st,
-                                              float scale_log2, int half, int lane) {
-  const int h32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // ---- partial S^T over latent tiles 2*half, 2*half+1 and rope dims 32*half..+31
-  f32x16 s = {};
-  const uint8_t* krow = tile + 16 * (32 * blk + h32) + 8 * hh;  // chunk c at + c * CS
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = 2 * half + tt;
-    f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(krow + (8 * t + kk) * CS);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen_fp8x8(raw.x, raw.y), qr[8 * tt + kk], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + t * TT + 32 * blk + 8 * qd + 4 * hh);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * qd + i] += sc[i] * acc[4 * qd + i];
-    }
-  }
-  {
-    // rope dims 32*half + 16*kk + 8*hh .. +7 are bytes 528 + 64*half + 32*kk + 16*hh
-    const uint8_t* rrow = tile + 16 * (32 * blk + h32) + (33 + 4 * half + hh) * CS;
-    f32x16 rp = {};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rrow + 2 * kk * CS);
-      rp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[16 + kk], rp, 0, 0, 0);
-    }
-    s += rp;
-  }
-
-  // ---- swap partial scores with the partner wave (same lane layout on both sides)
-#pragma unroll
-  for (int qd = 0; qd < 4; ++qd)
-    *reinterpret_cast<f32x4*>(xs_mine + 16 * lane + 4 * qd) =
-        f32x4{s[4 * qd], s[4 * qd + 1], s[4 * qd + 2], s[4 * qd + 3]};
-  __syncthreads();
-#pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(xs_peer + 16 * lane + 4 * qd);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[4 * qd + i] += v[i];  // a + b == b + a: both waves agree bit for bit
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tok = 8 * (r >> 2) + 4 * hh + (r & 3);
-    s[r] = tok < nvalid ? s[r] * scale_log2 : -INFINITY;
-  }
-
-  // ---- online softmax (lane = one head, 16 of the block's tokens)
-  float mx = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m_run, mx);
-  const bool need = m_new > st.m_run + kLazyRescale;
-  if (__any(need && st.m_run != -INFINITY)) {
-    const float alpha = need ? fast_exp2(st.m_run - m_new) : 1.0f;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) st.o[mb] *= alpha;
-    st.l_run *= alpha;
-  }
-  if (need) st.m_run = m_new;
-  const float mref = st.m_run == -INFINITY ? 0.0f : st.m_run;
-  float lsum = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s[r] = fast_exp2(s[r] - mref);
-    lsum += s[r];
-  }
-  st.l_run += lsum;
-
-  // ---- O^T += V^T P'^T over this wave's latent tiles
-  // tr8 row of lane (G = lane/16, rho = lane%16): token tau(ks, G/2, rho/2) and dims
-  // 128t + 32mb + 16(G%2) + 8(rho%2) .. +7, i.e. chunk 8t + 2mb + G%2 at byte 8(rho%2).
-  const int G = lane >> 4, rho = lane & 15, jj = rho >> 1;
-  const int tok0 = 8 * (jj >> 2) + 4 * (G >> 1) + (jj & 3);
-  const uint8_t* vbase = tile + 16 * (32 * blk + tok0) + (G & 1) * CS + 8 * (rho & 1);
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = 2 * half + tt;
-    f32x4 sc[4];
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      sc[qd] = *reinterpret_cast<const f32x4*>(sct + t * TT + 32 * blk + 8 * qd + 4 * hh);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 b;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = (__bf16)(s[8 * ks + j] * sc[2 * ks + (j >> 2)][j & 3]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const uint8_t* vp = vbase + 16 * 16 * ks + (8 * t + 2 * mb) * CS;
-        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS i32x2*)(vp));
-        st.o[4 * tt + mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            widen_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]), b, st.o[4 * tt + mb], 0, 0, 0);
-      }
-    }
-  }
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
 }
 
-// HBM -> LDS copy of one tile: lane r carries record r (records past the end of the list
-// repeat the last valid one) and load j moves chunk j of every record.  Wave w issues
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four fp32 values -> packed e4m3 hi terms and the exact residual lo terms.
+__device__ __forceinline__ void split_e4m3(float x0, float x1, float x2, float x3, int& hi, int& lo) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+  const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b01[0], x1 - b01[1], 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b23[0], x3 - b23[1], l, true);
+  hi = h;
+  lo = l;
+}
+
+// HBM -> LDS copy of one tile: lane r < TT carries record r (records past the end of the
+// list repeat the last valid one) and load j moves chunk j of every record.  Wave w issues
 // chunks w, w + NW, ...
-template <int NW>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, int wave) {
+template <int NW, int TT>
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, int wave, int lane) {
+  if (lane < TT) {
 #pragma unroll
-  for (int k = 0; k < (41 + NW - 1) / NW; ++k) {
-    const int j = k * NW + wave;
-    if (j < 41) __builtin_amdgcn_global_load_lds(rec + 16 * j, (SMLA_LDS void*)(stage + j * CS), 16, 0, 0);
+    for (int k = 0; k < (41 + NW - 1) / NW; ++k) {
+      const int j = k * NW + wave;
+      if (j < 41) __builtin_amdgcn_global_load_lds(rec + 16 * j, (SMLA_LDS void*)(stage + j * 16 * TT), 16, 0, 0);
+    }
   }
 }
 
-template <int NP>
-__global__ __launch_bounds__(NP * 128, 1) void decode_kernel(DecodeParams p) {
-  constexpr int NW = 2 * NP;
+template <int NW, int TT>
+__global__ __launch_bounds__(NW * 64, 1) void decode_kernel(DecodeParams p) {
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStageBytes];
+  constexpr int NB = TT / 32;        // 32-token blocks per tile
+  constexpr int CS = 16 * TT;        // bytes per chunk row of a tile
+  constexpr int DPW = kLatent / NW;  // output dims per wave
+  constexpr int NDB = DPW / 32;      // 32-dim output blocks per wave
+  constexpr int TPW = 4 / NW;        // scale tiles per wave
+  constexpr int HPB = 32 * NW;       // heads per workgroup
+  constexpr int PS = 2 * TT;         // bytes per head row of a probability tile
+  constexpr int GM = TT / 8 - 1;     // 16-byte granules of a row are XOR-swizzled by head & GM
+  constexpr int PT = HPB * PS;       // bytes per scale tile of probabilities
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[41 * CS];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[41 * CS];
   __shared__ __attribute__((aligned(16))) float sct[4 * TT];
-  __shared__ __attribute__((aligned(16))) float xs[2][NW][64 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[4 * PT];
+  __shared__ float linv_s[HPB];
   __shared__ int32_t clist[kMaxEntriesPerSplit];
   __shared__ int32_t wave_cnt[NW];
   __shared__ int32_t last_flag;
@@ -210,12 +131,9 @@ __global__ __launch_bounds__(NP * 128, 1) void decode_kernel(DecodeParams p) {
   const int lane = tid & 63;
   const int h32 = lane & 31;
   const int hh = lane >> 5;
-  const int pair = wave >> 1;
-  const int half = wave & 1;
 
   // Consecutive blocks are dispatched round-robin over the 8 XCDs; give every XCD a
-  // contiguous range of work items so that the head blocks and splits of a row, which
-  // gather the same records, run side by side on one XCD and share its L2.
+  // contiguous range of work items so the splits of a row run side by side on one XCD.
   const int per_xcd = (int)((gridDim.x + 7) / 8);
   const int wg = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (wg >= p.T * p.head_blocks * p.splits) return;
@@ -223,23 +141,68 @@ __global__ __launch_bounds__(NP * 128, 1) void decode_kernel(DecodeParams p) {
   const int rest = wg / p.splits;
   const int hb = rest % p.head_blocks;
   const int row = rest / p.head_blocks;
-  const int head = hb * p.heads_per_block + pair * kHeadsPerWave + h32;
-  const bool head_ok = head < p.H && (pair * kHeadsPerWave + h32) < p.heads_per_block;
+  const int h_lo = hb * HPB;
+  const int qhead = h_lo + wave * 32 + h32;  // head whose scores this lane computes
+  const bool q_ok = qhead < p.H;
 
-  // ---- query fragments: latent dims 256*half + 16k + 8*hh (k < 16), rope dims 32*half + 16k + 8*hh
-  bf16x8 qr[18];
+  // ---- query: latent as exact e4m3 pairs (dims 128t + 64kk + 32hh + i <-> byte i), rope bf16
+  i32x8 qh[4][2], ql[4][2];
+  bf16x8 qr[4];
+  float qexp_inv;  // 2^-e_h (the rope fragments carry the same 2^e_h)
   {
-    const int hc = head_ok ? head : 0;
-    const uint16_t* qp = p.q + (int64_t)row * p.q_st + (int64_t)hc * p.q_sh + 8 * hh;
+    const uint16_t* qp = p.q + (int64_t)row * p.q_st + (int64_t)(q_ok ? qhead : 0) * p.q_sh + 32 * hh;
+    // pass 1: per-head max |q| over the latent dims (lanes h32 and h32 + 32 hold one head)
+    float amax = 0.0f;
+    if (q_ok) {
+#pragma unroll 4
+      for (int c = 0; c < 32; ++c) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 64 * (c >> 2) + 8 * (c & 3));
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 256 * half + 16 * k);
-      qr[k] = head_ok ? v : bf16x8{};
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
+      }
     }
+    if (q_ok) {
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh + 8);
+      const bf16x8 v2 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh + 16);
+      const bf16x8 v3 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh + 24);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * half + 16 * k);
-      qr[16 + k] = head_ok ? v : bf16x8{};
+      for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf((float)v0[i]), fabsf((float)v1[i])),
+                                 fmaxf(fabsf((float)v2[i]), fabsf((float)v3[i]))));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    int e = 0;
+    if (amax > 0.0f) {
+      e = (int)floorf(__log2f(448.0f / amax));
+      if (ldexpf(amax, e) > 448.0f) --e;
+      e = max(-100, min(100, e));
+    }
+    qexp_inv = ldexpf(1.0f, -e);
+    // pass 2: q * 2^e = hi + lo, both e4m3 (exact for |q * 2^e| >= 2^-2, see the design notes)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 v = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 128 * t + 64 * kk + 8 * c) : bf16x8{};
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            int hi, lo;
+            split_e4m3(ldexpf((float)v[4 * g], e), ldexpf((float)v[4 * g + 1], e), ldexpf((float)v[4 * g + 2], e),
+                       ldexpf((float)v[4 * g + 3], e), hi, lo);
+            qh[t][kk][2 * c + g] = hi;
+            ql[t][kk][2 * c + g] = lo;
+          }
+        }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 v = q_ok ? *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 16 * kk + 8 * hh) : bf16x8{};
+      bf16x8 w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = (__bf16)ldexpf((float)v[i], e);  // exact: |q * 2^e| <= 448
+      qr[kk] = w;
     }
   }
 
@@ -280,86 +243,198 @@ __global__ __launch_bounds__(NP * 128, 1) void decode_kernel(DecodeParams p) {
     __syncthreads();
   }
 
-  // ---- main loop over gathered tiles
-  WaveState st;
+  // ---- state: O^T accumulators o[db][hg] = dims wave*DPW + 32db + 8(r/4) + 4hh + r%4, head h_lo + 32hg + h32
+  f32x16 o[NDB][NW];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) st.o[mb] = f32x16{};
-  st.m_run = -INFINITY;
-  st.l_run = 0.0f;
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int hg = 0; hg < NW; ++hg) o[db][hg] = f32x16{};
+  float m_ref = -INFINITY;  // reference max of head qhead (log2 units), same in lanes h32 and h32+32
+  float m_max = -INFINITY;  // exact running max of head qhead
+  float l_run = 0.0f;       // this lane's share of the softmax sum of head qhead
+
+  const float sl_lat = p.scale_log2 * qexp_inv;
 
   const int ntiles = (total + TT - 1) / TT;
-  int xbuf = 0;
-  if (ntiles > 0) issue_tile<NW>(stage0, p.kv + (int64_t)clist[min(lane, total - 1)] * kRecordBytes, wave);
+  for (int pass = 0; pass < 2; ++pass) {
+  bool over = false;  // a score exceeded the reference by more than the headroom
+  if (ntiles > 0) issue_tile<NW, TT>(stage0, p.kv + (int64_t)clist[min(lane, total - 1)] * kRecordBytes, wave, lane);
   for (int it = 0; it < ntiles; ++it) {
-    uint8_t* cur = (it & 1) ? stage1 : stage0;
-    // the loads of tile `it` are this wave's only ones in flight
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile `it` is in LDS and every wave is done with tile it-1
+    uint8_t* tile = (it & 1) ? stage1 : stage0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile `it`
+    __syncthreads();  // tile `it` in LDS; every wave is done with tile it-1 (its probabilities included)
     if (it + 1 < ntiles) {
       const int idx = min((it + 1) * TT + lane, total - 1);
-      issue_tile<NW>((it & 1) ? stage0 : stage1, p.kv + (int64_t)clist[idx] * kRecordBytes, wave);
+      issue_tile<NW, TT>((it & 1) ? stage0 : stage1, p.kv + (int64_t)clist[idx] * kRecordBytes, wave, lane);
     }
     // scale chunk (chunk 32) is [record][4 fp32]; transpose it to [tile][record]
     for (int i = tid; i < 4 * TT; i += NT) {
       const int tok = i >> 2, t = i & 3;
-      sct[t * TT + tok] = *reinterpret_cast<const float*>(cur + 32 * CS + 16 * tok + 4 * t);
+      sct[t * TT + tok] = *reinterpret_cast<const float*>(tile + 32 * CS + 16 * tok + 4 * t);
     }
     __syncthreads();
     const int nin = min(TT, total - it * TT);
+
+    // ---- per 32-token block: scores of this wave's 32 heads, softmax numerators, P'
+    // s[r] <-> token 32b + 8(r/4) + 4hh + r%4 of the tile; lane = head qhead
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));  // recompute lane-derived addresses here instead of hoisting them
+    const int l32 = lane_o & 31, lhh = lane_o >> 5;
 #pragma unroll
-    for (int b = 0; b < TT / 32; ++b) {
-      if (32 * b < nin) {
-        block_compute(cur, sct, xs[xbuf][wave], xs[xbuf][wave ^ 1], b, nin - 32 * b, qr, st, p.scale_log2, half,
-                      lane);
-        xbuf ^= 1;
+    for (int b = 0; b < NB; ++b) {
+      if (32 * b >= nin) break;
+      const uint8_t* krow = tile + 16 * (32 * b + l32);
+      // rope dims 16kk + 8hh .. +7 (bf16, both operands scaled by 2^e_h): chunk 33 + 2kk + hh
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(krow + (33 + 2 * kk + lhh) * CS), qr[kk], s);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int c0 = 8 * t + 4 * kk + 2 * lhh;  // dims 128t + 64kk + 32hh .. +31
+          const i32x4 a0 = *reinterpret_cast<const i32x4*>(krow + c0 * CS);
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(krow + (c0 + 1) * CS);
+          const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          acc = mfma_fp8(a, qh[t][kk], acc);
+          acc = mfma_fp8(a, ql[t][kk], acc);
+        }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + t * TT + 32 * b + 8 * qd + 4 * lhh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[4 * qd + i] += sc[i] * acc[4 * qd + i];
+        }
+      }
+      s *= sl_lat;
+      if (nin - 32 * b < 32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * lhh + (r & 3) >= nin - 32 * b) s[r] = -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_max = fmaxf(m_max, mx);
+      if (m_ref == -INFINITY) m_ref = mx;
+      over |= mx > m_ref + kRefHeadroom;
+      const float mref = m_ref == -INFINITY ? 0.0f : m_ref;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = fast_exp2(s[r] - mref);
+        lsum += s[r];
+      }
+      l_run += lsum;
+      // P'_t = bf16(p * scale(token, t)) as [t][head][token]; granule tok/8 = 4b + qd, byte 8hh inside it
+      const int ph = wave * 32 + l32;
+      uint8_t* prow = pbuf + ph * PS + 8 * lhh;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + t * TT + 32 * b + 8 * qd + 4 * lhh);
+          const bf16x4 v = {(__bf16)(s[4 * qd] * sc[0]), (__bf16)(s[4 * qd + 1] * sc[1]),
+                            (__bf16)(s[4 * qd + 2] * sc[2]), (__bf16)(s[4 * qd + 3] * sc[3])};
+          *reinterpret_cast<bf16x4*>(prow + t * PT + 16 * ((4 * b + qd) ^ (ph & GM))) = v;
+        }
+    }
+    __syncthreads();
+
+    // ---- O^T += V^T P'^T for this wave's dims and every head of the workgroup
+#pragma unroll
+    for (int ks = 0; ks < TT / 16; ++ks) {
+      if (16 * ks < nin) {
+        bf16x8 bq[TPW][NW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+          for (int hg = 0; hg < NW; ++hg)
+            bq[tt][hg] = *reinterpret_cast<const bf16x8*>(pbuf + (wave * TPW + tt) * PT + (32 * hg + l32) * PS +
+                                                          16 * ((2 * ks + lhh) ^ ((32 * hg + l32) & GM)));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int mbg = wave * NDB + db;  // global 32-dim block: chunks 2mbg, 2mbg+1
+          const int vrow = 16 * (8 * ((lane_o >> 4) >> 1) + ((lane_o & 15) >> 1)) + 8 * (lane_o & 1) +
+                           ((lane_o >> 4) & 1) * CS;  // tr8 row of this lane
+          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (SMLA_LDS i32x2*)(tile + 2 * mbg * CS + 16 * 16 * ks + vrow));
+          const bf16x8 va = widen_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
+          const int tt = db / 4;  // 4 dim blocks per scale tile
+#pragma unroll
+          for (int hg = 0; hg < NW; ++hg) o[db][hg] = mfma_bf16(va, bq[tt][hg], o[db][hg]);
+        }
       }
     }
   }
 
-  // ---- epilogue
-  const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-  const int dbase = 256 * half + 4 * hh;  // + 32*mb + 8*qd
+  // a second pass, with the exact max as reference, only if some score outgrew the headroom
+  if (!__syncthreads_or(over)) break;
+  m_ref = m_max;
+  l_run = 0.0f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int hg = 0; hg < NW; ++hg) o[db][hg] = f32x16{};
+  }  // pass
+
+  // ---- epilogue: per-head sums from the score waves, normalisation by the value waves
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  __syncthreads();  // every wave is done reading pbuf
+  if (hh == 0) linv_s[wave * 32 + h32] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (p.splits == 1 && q_ok && hh == 0)
+    p.lse[(int64_t)row * p.l_st + (int64_t)qhead * p.l_sh] =
+        l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (p.splits > 1 && q_ok && hh == 0) {
+    const int64_t pidx = ((int64_t)row * p.splits + split) * p.H + qhead;
+    p.ws_ml[pidx * 2 + 0] = l_tot > 0.0f ? m_ref : -INFINITY;
+    p.ws_ml[pidx * 2 + 1] = l_tot;
+  }
+  __syncthreads();
+  const int dbase = wave * DPW + 4 * hh;  // + 32db + 8qd
   if (p.splits == 1) {
-    if (!head_ok) return;
-    const bool empty = !(l_tot > 0.0f);
-    const float inv = empty ? 0.0f : 1.0f / l_tot;
-    if (p.out_fp32) {
-      float* orow = reinterpret_cast<float*>(p.out) + (int64_t)row * p.o_st + (int64_t)head * p.o_sh + dbase;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+    for (int hg = 0; hg < NW; ++hg) {
+      const int head = h_lo + 32 * hg + h32;
+      if (head >= p.H) continue;
+      const float inv = linv_s[32 * hg + h32];
+      if (p.out_fp32) {
+        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)row * p.o_st + (int64_t)head * p.o_sh + dbase;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<f32x4*>(orow + 32 * mb + 8 * qd) =
-              f32x4{st.o[mb][4 * qd], st.o[mb][4 * qd + 1], st.o[mb][4 * qd + 2], st.o[mb][4 * qd + 3]} * inv;
-    } else {
-      __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)row * p.o_st + (int64_t)head * p.o_sh + dbase;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd) =
+                f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
+      } else {
+        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)row * p.o_st + (int64_t)head * p.o_sh + dbase;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<bf16x4*>(orow + 32 * mb + 8 * qd) =
-              bf16x4{(__bf16)(st.o[mb][4 * qd] * inv), (__bf16)(st.o[mb][4 * qd + 1] * inv),
-                     (__bf16)(st.o[mb][4 * qd + 2] * inv), (__bf16)(st.o[mb][4 * qd + 3] * inv)};
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * qd) =
+                bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
+                       (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
+      }
     }
-    if (half == 0 && hh == 0)
-      p.lse[(int64_t)row * p.l_st + (int64_t)head * p.l_sh] = empty ? -INFINITY : (st.m_run + __log2f(l_tot)) * kLn2;
     return;
   }
 
-  // ---- split-K: publish this split's partial, the last arrival combines
-  if (head_ok) {
-    const int64_t pidx = ((int64_t)row * p.splits + split) * p.H + head;
-    float* po = p.ws_o + pidx * kLatent + dbase;
+  // ---- split-K: publish this split's unnormalised partial, the last arrival combines
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+  for (int hg = 0; hg < NW; ++hg) {
+    const int head = h_lo + 32 * hg + h32;
+    if (head >= p.H) continue;
+    float* po = p.ws_o + (((int64_t)row * p.splits + split) * p.H + head) * kLatent + dbase;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<f32x4*>(po + 32 * mb + 8 * qd) =
-            f32x4{st.o[mb][4 * qd], st.o[mb][4 * qd + 1], st.o[mb][4 * qd + 2], st.o[mb][4 * qd + 3]};
-    if (half == 0 && hh == 0) {
-      p.ws_ml[pidx * 2 + 0] = l_tot > 0.0f ? st.m_run : -INFINITY;
-      p.ws_ml[pidx * 2 + 1] = l_tot;
-    }
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd) =
+            f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]};
   }
   __threadfence();
   __syncthreads();
@@ -372,8 +447,7 @@ __global__ __launch_bounds__(NP * 128, 1) void decode_kernel(DecodeParams p) {
   if (!last_flag) return;
   __threadfence();
 
-  const int h_lo = hb * p.heads_per_block;
-  const int nh = min(p.heads_per_block, p.H - h_lo);
+  const int nh = min(HPB, p.H - h_lo);
   for (int item = tid; item < nh * (kLatent / 4); item += NT) {
     const int hrel = item / (kLatent / 4);
     const int d4 = item - hrel * (kLatent / 4);
@@ -400,8 +474,7 @@ __global__ __launch_bounds__(NP * 128, 1) void decode_kernel(DecodeParams p) {
       *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc;
     } else {
       __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<bf16x4*>(orow + 4 * d4) =
-          bf16x4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+      *reinterpret_cast<bf16x4*>(orow + 4 * d4) = bf16x4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
     }
     if (d4 == 0) p.lse[(int64_t)row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
   }
@@ -424,11 +497,14 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStrea
     hipLaunchKernelGGL(zero_counters, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.ws_cnt, n);
   }
   switch (plan.waves) {
+    case 1:
+      hipLaunchKernelGGL((decode_kernel<1, 32>), dim3(grid), dim3(64), 0, stream, p);
+      break;
     case 2:
-      hipLaunchKernelGGL((decode_kernel<1>), dim3(grid), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((decode_kernel<2, 32>), dim3(grid), dim3(128), 0, stream, p);
       break;
     case 4:
-      hipLaunchKernelGGL((decode_kernel<2>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_kernel<4, 64>), dim3(grid), dim3(256), 0, stream, p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -29,24 +29,24 @@ int device_cus() {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split plan for a decode call.  A workgroup holds one wave per SIMD and owns up to 64
-// heads of one row (a wave pair per 32 heads); its LDS footprint allows one workgroup per
-// CU.  Rows are cut into top-k ranges only when rows x head blocks cannot cover every CU.
+// Split plan for a decode call.  A workgroup holds one wave per SIMD, 32 heads per wave
+// (1, 2 or 4 waves: up to 128 heads of one row); with 4 waves its LDS footprint allows one
+// workgroup per CU, with 1 or 2 waves two.  Rows are cut into top-k ranges only when rows
+// cannot cover every workgroup slot of the device.
 DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cus) {
   DecodePlan pl{};
-  const int pairs = H > kHeadsPerWave ? 2 : 1;
-  pl.waves = 2 * pairs;
-  const int hpb = pairs * kHeadsPerWave;
-  pl.head_blocks = (H + hpb - 1) / hpb;
+  pl.waves = H <= 32 ? 1 : (H <= 64 ? 2 : 4);
+  pl.head_blocks = 1;
   const int min_splits = K > 0 ? (K + kMaxEntriesPerSplit - 1) / kMaxEntriesPerSplit : 1;
   int splits;
   if (num_splits > 0) {
     splits = num_splits;
   } else {
     const int64_t wgs = (int64_t)T * pl.head_blocks;
+    const int64_t slots = (int64_t)cus * (pl.waves == 4 ? 1 : 2);
     splits = 1;
-    if (wgs > 0 && wgs < cus) {
-      const int64_t want = (cus + wgs - 1) / wgs;
+    if (wgs > 0 && wgs < slots) {
+      const int64_t want = (slots + wgs - 1) / wgs;
       const int64_t cap = K / 256 > 1 ? K / 256 : 1;  // keep >= 256 entries (4 tiles) per split
       splits = (int)(want < cap ? want : cap);
     }
@@ -175,7 +175,7 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
   p.splits = plan.splits;
   p.entries_per_split = plan.entries_per_split;
   p.head_blocks = plan.head_blocks;
-  p.heads_per_block = (plan.waves / 2) * kHeadsPerWave;
+  p.heads_per_block = plan.waves * kHeadsPerWave;
   if (plan.ws_total > 0) {
     char* ws = static_cast<char*>(workspace);
     p.ws_cnt = reinterpret_cast<int32_t*>(ws);
