@@ -82,6 +82,29 @@ def cpu_baseline(w, budget_s):
                       f"shard attention, LSE merge), {dt:.1f} s on {os.cpu_count()} host CPUs"}
 
 
+# HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
+# read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
+DECODE_TRAFFIC = {"sources_sha256": None, "fetch_bytes": None, "write_bytes": None}
+KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    t = DECODE_TRAFFIC
+    if t["sources_sha256"] is None or t["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return int(t["fetch_bytes"] + t["write_bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +113,10 @@ def main():
     ap.add_argument("--replicas", type=int, default=2, help="cache copies rotated between steps (beat the 256 MB MALL)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unsharded", action="store_true",
+                    help="also time the unsharded decode of the same rows (reported beside the step)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
@@ -116,8 +143,9 @@ def main():
     ids = torch.from_numpy(w.ids).to(dev)
     req = torch.from_numpy(w.req).to(dev)
     replicas = [device_shards(w, dev) for _ in range(max(1, args.replicas))]
-    unsharded_cache = w.cache.to_device(dev)
-    unsharded_bt = torch.from_numpy(w.block_table).to(dev)
+    if args.unsharded:
+        unsharded_cache = w.cache.to_device(dev)
+        unsharded_bt = torch.from_numpy(w.block_table).to(dev)
     torch.cuda.synchronize()
 
     step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=w.dcp_size, block_size=w.block_size,
@@ -161,27 +189,36 @@ def main():
     nv_mean = float(np.mean(shard_valid))
     byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, out_bytes=4)
     roof = roofline_entry(byts, flops, mean_dec_s)
-    roof["traffic"] = None
-    roof["kernel"] = "decode_kernel<2> (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
+    roof["traffic"] = measured_traffic()
+    roof["kernel"] = "decode_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
     roof["launch_us"] = round(mean_dec_s * 1e6, 2)
     roof["algorithmic_bytes"] = int(byts)
     roof["algorithmic_flops"] = int(flops)
     kv_gbps = 656 * sum(shard_valid) * args.steps / (float(np.sum(dec_ms)) / 1e3) / 1e9
 
-    # the unsharded H=128 / top-k 2048 decode of the same rows (reported beside the step)
-    one = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=1, block_size=w.block_size, softmax_scale=w.sm_scale,
-                        out_dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        one.run(q, ids, req, [(unsharded_cache, unsharded_bt)])
-    torch.cuda.synchronize()
-    decode_events.clear()
-    for _ in range(max(10, args.steps // 2)):
-        one.run(q, ids, req, [(unsharded_cache, unsharded_bt)], decode_events=decode_events)
-    torch.cuda.synchronize()
-    un_s = float(np.mean([a.elapsed_time(b) for a, b in decode_events])) / 1e3
-    ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], out_bytes=2)
-    unsharded = {"decode_us": round(un_s * 1e6, 2), "tflops": round(uf / un_s / 1e12, 1),
-                 "kv_gbps": round(656 * nvalid[0] / un_s / 1e9, 1), "roofline": roofline_entry(ub, uf, un_s)}
+    unsharded = None
+    if args.unsharded:  # the unsharded H=128 / top-k 2048 decode of the same rows
+        one = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=1, block_size=w.block_size, softmax_scale=w.sm_scale,
+                            out_dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            one.run(q, ids, req, [(unsharded_cache, unsharded_bt)])
+        torch.cuda.synchronize()
+        un_events = []
+        for _ in range(max(10, args.steps // 2)):
+            one.run(q, ids, req, [(unsharded_cache, unsharded_bt)], decode_events=un_events)
+        torch.cuda.synchronize()
+        un_s = float(np.mean([a.elapsed_time(b) for a, b in un_events])) / 1e3
+        ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], out_bytes=2)
+        unsharded = {"decode_us": round(un_s * 1e6, 2), "tflops": round(uf / un_s / 1e12, 1),
+                     "kv_gbps": round(656 * nvalid[0] / un_s / 1e9, 1), "roofline": roofline_entry(ub, uf, un_s)}
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     line = {
         "metric": METRIC, "value": round(rows_per_s, 1), "unit": "query-rows/s", "n_gpus": 1, "steps": args.steps,
@@ -193,8 +230,9 @@ def main():
                    "cache_replicas": len(replicas)},
         "kv_gbps": round(kv_gbps, 1),
         "roofline": roof,
-        "unsharded_decode": unsharded,
     }
+    if unsharded is not None:
+        line["unsharded_decode"] = unsharded
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

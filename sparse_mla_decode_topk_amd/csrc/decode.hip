@@ -6,34 +6,38 @@
 // "[eldritch] attention: support DCP in SM120 FlashInfer sparse MLA", "Why").
 //
 // gfx950 design
-//  * A workgroup owns one row, up to 128 heads (NW waves x 32) and one range of the row's
-//    top-k list, with one wave per SIMD.  Every gathered record feeds all heads of the row.
-//  * Work split inside the workgroup: wave w computes scores, softmax and probabilities for
-//    its 32 heads over all 576 dims; the probabilities go to LDS; wave w then accumulates
-//    output dims [w*512/NW, (w+1)*512/NW) for ALL heads of the workgroup.  No softmax is
-//    duplicated and every value operand is widened by exactly one wave.
+//  * A workgroup owns one row, up to 64 heads of it and one range of the row's top-k list.
+//    It runs 8 waves, two per SIMD, in two roles that overlap on every SIMD: four score
+//    waves (16 heads each) run QK^T on fp8 MFMA plus the softmax on the VALU for tile n,
+//    while four value waves (one 128-dim scale tile of the output each) run PV on bf16
+//    MFMA for tile n-1.  One SIMD thus interleaves one wave's vector work with the other's
+//    matrix work.  The query lives in the score waves' registers, the output accumulators
+//    in the value waves'; the roles branch apart at the top so neither holds the other's.
 //  * Gather: the row's slot range is compacted in LDS (-1 and out-of-range entries are
-//    skipped; no front-pack on the host), then tiles of TT records are copied HBM -> LDS
-//    with global_load_lds_dwordx4 (no register staging), double-buffered.  Lane r of a load
-//    carries record r of the tile and load j moves 16-byte chunk j of every record, so the
-//    tile sits in LDS chunk-major ([41 chunks][TT records][16 B]): one base address per
-//    lane, and every MFMA operand read below is a contiguous LDS access.
-//  * QK^T latent part on fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales): the raw
-//    e4m3 codes are the A operand as stored, and q is split exactly into two e4m3 terms,
+//    skipped; no front-pack on the host), then tiles of 32 records are copied HBM -> LDS
+//    with global_load_lds_dwordx4 by the value waves, kAhead tiles ahead.  One load moves
+//    two 16-byte chunks of all 32 records, so a tile sits chunk-major in LDS
+//    ([41 chunks][32 records][16 B]) and every MFMA operand read is contiguous.
+//  * QK^T latent part on v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales): the raw e4m3
+//    codes are the record operand as stored; q is split exactly into two e4m3 terms,
 //    q * 2^e_h = hi + lo (hi = rne(q * 2^e_h), lo = rne(q * 2^e_h - hi), e_h a per-head power
-//    of two putting max|q| just under 448), so two fp8 MFMAs give the bf16-exact product at
-//    the cost of one bf16 MFMA and no operand widening.  Each 128-dim fp32 record scale
-//    multiplies the fp32 partial dot product of its tile.  Rope dims (bf16) run on
-//    v_mfma_f32_32x32x16_bf16.  S^T (tokens x heads) puts one head per lane, so softmax row
-//    reductions are in-lane plus one cross-half swap.
+//    of two that puts max|q| just under 448; exact wherever |q * 2^e_h| >= 2^-2), so two fp8
+//    MFMAs give the bf16-exact product at the cost of one bf16 MFMA and no widening.  One
+//    MFMA k-step spans exactly one 128-dim scale tile, whose fp32 record scale then
+//    multiplies that tile's partial dot product.  Rope dims (bf16) run on
+//    v_mfma_f32_16x16x32_bf16.  Scores come out as S^T (tokens x heads): one head per lane.
 //  * Softmax in base 2 against a per-head reference max fixed at the first tile: later
 //    probabilities are 2^(s - ref) and may exceed 1, which fp32 accumulators and bf16
 //    probabilities hold without loss.  Should a score ever exceed the reference by more
-//    than 2^64 the workgroup recomputes the row once with the exact max as reference, so
-//    the accumulators are never rescaled inside the loop.
-//  * PV: O^T[dim, head] += V^T[dim, token] . P'^T[token, head] on bf16 MFMA with
-//    P' = p * scale(token, tile) rounded once to bf16 (written to LDS per scale tile); V^T
-//    fragments come from the tile through ds_read_b64_tr_b8 and are widened exactly.
+//    than 2^64 the workgroup recomputes the range once with the exact max as reference, so
+//    the output accumulators are never rescaled inside the loop and the value waves never
+//    wait on a max.
+//  * PV: O^T[dim, head] += V^T[dim, token] . P'^T[token, head] on bf16 MFMA, with
+//    P' = p * scale(token, tile) rounded once to bf16 and handed over in LDS per scale tile
+//    (double-buffered); V^T fragments come straight from the staged tile through
+//    ds_read_b64_tr_b8 and are widened exactly.
+//  * One workgroup barrier per tile orders it all: tile n staged, P'(n-1) written, and
+//    tile n-2 plus P'(n-2) consumed, so its buffers may be refilled.
 //  * Split-K over the top-k list with an in-kernel combine: every split writes its
 //    unnormalised partial (O, max, sum) to the workspace; the last split to arrive (device
 //    scope counter, zeroed by a small kernel before the decode kernel) merges them.
@@ -61,6 +65,33 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRefHeadroom = 64.0f;  // log2 units a score may exceed the reference by
 constexpr int kUnitScale = 127;       // E8M0 encoding of 2^0 for the scaled fp8 MFMA
 
+constexpr int kThreads = 512;                   // 4 score waves + 4 value waves
+constexpr int kTT = 32;                         // records per tile
+constexpr int kChunks = kRecordBytes / 16;      // 41 chunks of 16 bytes per record
+constexpr int kCS = 16 * kTT;                   // bytes per chunk row of a tile
+constexpr int kTileBytes = kChunks * kCS;       // 20992
+constexpr int kStages = 4;                      // tile buffers: scores on n, values on n-1,
+constexpr int kAhead = kStages - 2;             //   loads in flight for n+1 .. n+kAhead
+constexpr int kLoads = (kChunks + 1) / 2;       // 21 global_load_lds per tile, two chunks each
+constexpr int kHB = kHeadsPerBlock;             // 64 heads per workgroup
+constexpr int kPRow = 2 * kTT;                  // bytes per head row of a probability tile
+constexpr int kPTile = kHB * kPRow;             // one scale tile of probabilities (4 KB)
+constexpr int kPBuf = 4 * kPTile;               // all four scale tiles (16 KB)
+constexpr int kScaleChunk = kScaleOffset / 16;  // 32
+constexpr int kRopeChunk = kRopeOffset / 16;    // 33
+
+static_assert(kRecordBytes % 16 == 0, "records are whole 16-byte chunks");
+static_assert(kAhead >= 1 && kAhead <= 3, "load waits below cover up to 3 tiles ahead");
+
+struct Shared {
+  uint8_t stage[kStages * kTileBytes];
+  uint8_t pbuf[2 * kPBuf];
+  int32_t clist[kMaxEntriesPerSplit];
+  float ml[2 * kHB];  // per head of the block: (reference max, sum)
+  int32_t wave_cnt[kThreads / 64];
+  int32_t last_flag;
+};
+
 __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
   const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
@@ -71,11 +102,15 @@ __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+__device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
 }
 
-__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+__device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
@@ -91,86 +126,80 @@ __device__ __forceinline__ void split_e4m3(float x0, float x1, float x2, float x
   lo = l;
 }
 
-// HBM -> LDS copy of one tile: lane r < TT carries record r (records past the end of the
-// list repeat the last valid one) and load j moves chunk j of every record.  Wave w issues
-// chunks w, w + NW, ...
-template <int NW, int TT>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, int wave, int lane) {
-  if (lane < TT) {
-#pragma unroll
-    for (int k = 0; k < (41 + NW - 1) / NW; ++k) {
-      const int j = k * NW + wave;
-      if (j < 41) __builtin_amdgcn_global_load_lds(rec + 16 * j, (SMLA_LDS void*)(stage + j * 16 * TT), 16, 0, 0);
-    }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Global->LDS loads one value wave issues per tile: load j of a tile belongs to wave j % 4.
+__device__ __forceinline__ int loads_of_wave(int b) { return b < kLoads % 4 ? kLoads / 4 + 1 : kLoads / 4; }
+
+// Wait until this wave's loads of tile n have landed, given `tiles_newer` later tiles of
+// this wave still in flight (wave-uniform).
+__device__ __forceinline__ void wait_tile(int tiles_newer, int b) {
+  const int newer = tiles_newer * loads_of_wave(b);
+  switch (newer) {
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    default: wait_vmcnt<0>(); break;
   }
 }
 
-template <int NW, int TT>
-__global__ __launch_bounds__(NW * 64, 1) void decode_kernel(DecodeParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int NB = TT / 32;        // 32-token blocks per tile
-  constexpr int CS = 16 * TT;        // bytes per chunk row of a tile
-  constexpr int DPW = kLatent / NW;  // output dims per wave
-  constexpr int NDB = DPW / 32;      // 32-dim output blocks per wave
-  constexpr int TPW = 4 / NW;        // scale tiles per wave
-  constexpr int HPB = 32 * NW;       // heads per workgroup
-  constexpr int PS = 2 * TT;         // bytes per head row of a probability tile
-  constexpr int GM = TT / 8 - 1;     // 16-byte granules of a row are XOR-swizzled by head & GM
-  constexpr int PT = HPB * PS;       // bytes per scale tile of probabilities
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[41 * CS];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[41 * CS];
-  __shared__ __attribute__((aligned(16))) float sct[4 * TT];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[4 * PT];
-  __shared__ float linv_s[HPB];
-  __shared__ int32_t clist[kMaxEntriesPerSplit];
-  __shared__ int32_t wave_cnt[NW];
-  __shared__ int32_t last_flag;
+// HBM -> LDS copy of one tile by value wave b (0..3): load j moves chunks 2j and 2j+1 of all
+// 32 records (lane r < 32: chunk 2j of record r, lane 32 + r: chunk 2j + 1 of record r), so
+// its LDS destination is the contiguous kilobyte j of the tile.  `rec` is this lane's record
+// (plus 16 bytes in the upper half-wave).
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, int b, int lane) {
+#pragma unroll
+  for (int k = 0; k < (kLoads + 3) / 4; ++k) {
+    const int j = b + 4 * k;
+    if (j < kLoads - 1 || (j == kLoads - 1 && lane < 32))
+      __builtin_amdgcn_global_load_lds(rec + 32 * j, (SMLA_LDS void*)(stage + 1024 * j), 16, 0, 0);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-  const int lane = tid & 63;
-  const int h32 = lane & 31;
-  const int hh = lane >> 5;
+// Record of tile entry (lane & 31); entries past the end of the list repeat the last one.
+__device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, const Shared& sh, int n, int total,
+                                                      int lane) {
+  const int idx = min(n * kTT + (lane & 31), total - 1);
+  return p.kv + (int64_t)sh.clist[idx] * kRecordBytes + 16 * (lane >> 5);
+}
 
-  // Consecutive blocks are dispatched round-robin over the 8 XCDs; give every XCD a
-  // contiguous range of work items so the splits of a row run side by side on one XCD.
-  const int per_xcd = (int)((gridDim.x + 7) / 8);
-  const int wg = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (wg >= p.T * p.head_blocks * p.splits) return;
-  const int split = wg % p.splits;
-  const int rest = wg / p.splits;
-  const int hb = rest % p.head_blocks;
-  const int row = rest / p.head_blocks;
-  const int h_lo = hb * HPB;
-  const int qhead = h_lo + wave * 32 + h32;  // head whose scores this lane computes
-  const bool q_ok = qhead < p.H;
+struct Block {
+  int row, hb, split, h_lo, nh, total, ntiles;
+};
 
-  // ---- query: latent as exact e4m3 pairs (dims 128t + 64kk + 32hh + i <-> byte i), rope bf16
-  i32x8 qh[4][2], ql[4][2];
-  bf16x8 qr[4];
-  float qexp_inv;  // 2^-e_h (the rope fragments carry the same 2^e_h)
-  {
-    const uint16_t* qp = p.q + (int64_t)row * p.q_st + (int64_t)(q_ok ? qhead : 0) * p.q_sh + 32 * hh;
-    // pass 1: per-head max |q| over the latent dims (lanes h32 and h32 + 32 hold one head)
+// ---------------------------------------------------------------------------------------
+// Score wave `sw` (0..3): heads h_lo + 16sw + (lane & 15); lane group g = lane >> 4 holds
+// the query dims 128t + 32g .. +31 of every scale tile t and rope dims 32kk + 8g .. +7.
+__device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, const Block& bk, int sw, int lane) {
+  const int g = lane >> 4;
+  const int hl = 16 * sw + (lane & 15);  // head within the block
+  const bool active = 16 * sw < bk.nh;
+  i32x8 qh[4], ql[4];  // q * 2^e as e4m3 hi / lo: byte i of tile t <-> dim 128t + 32g + i
+  bf16x8 qr[2];        // rope q * 2^e: element i of kk <-> rope dim 32kk + 8g + i
+  float cq = 0.0f;     // softmax_scale * log2(e) * 2^-e
+  if (active) {
+    const uint16_t* qp = p.q + (int64_t)bk.row * p.q_st + (int64_t)(bk.h_lo + hl) * p.q_sh;
+    // pass 1: per-head max |q| (lanes l, l^16, l^32, l^48 hold one head)
     float amax = 0.0f;
-    if (q_ok) {
-#pragma unroll 4
-      for (int c = 0; c < 32; ++c) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 64 * (c >> 2) + 8 * (c & 3));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 128 * t + 32 * g + 8 * c);
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
       }
-    }
-    if (q_ok) {
-      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh + 8);
-      const bf16x8 v2 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh + 16);
-      const bf16x8 v3 = *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 32 * hh + 24);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf((float)v0[i]), fabsf((float)v1[i])),
-                                 fmaxf(fabsf((float)v2[i]), fabsf((float)v3[i]))));
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * kk + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     int e = 0;
     if (amax > 0.0f) {
@@ -178,281 +207,248 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_kernel(DecodeParams p) {
       if (ldexpf(amax, e) > 448.0f) --e;
       e = max(-100, min(100, e));
     }
-    qexp_inv = ldexpf(1.0f, -e);
-    // pass 2: q * 2^e = hi + lo, both e4m3 (exact for |q * 2^e| >= 2^-2, see the design notes)
+    cq = p.scale_log2 * ldexpf(1.0f, -e);
+    // pass 2: q * 2^e = hi + lo, both e4m3
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 128 * t + 32 * g + 8 * c);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 v = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 128 * t + 64 * kk + 8 * c) : bf16x8{};
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            int hi, lo;
-            split_e4m3(ldexpf((float)v[4 * g], e), ldexpf((float)v[4 * g + 1], e), ldexpf((float)v[4 * g + 2], e),
-                       ldexpf((float)v[4 * g + 3], e), hi, lo);
-            qh[t][kk][2 * c + g] = hi;
-            ql[t][kk][2 * c + g] = lo;
-          }
+        for (int hf = 0; hf < 2; ++hf) {
+          int hi, lo;
+          split_e4m3(ldexpf((float)v[4 * hf], e), ldexpf((float)v[4 * hf + 1], e), ldexpf((float)v[4 * hf + 2], e),
+                     ldexpf((float)v[4 * hf + 3], e), hi, lo);
+          qh[t][2 * c + hf] = hi;
+          ql[t][2 * c + hf] = lo;
         }
+      }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 v = q_ok ? *reinterpret_cast<const bf16x8*>(qp - 32 * hh + kLatent + 16 * kk + 8 * hh) : bf16x8{};
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * kk + 8 * g);
       bf16x8 w;
 #pragma unroll
       for (int i = 0; i < 8; ++i) w[i] = (__bf16)ldexpf((float)v[i], e);  // exact: |q * 2^e| <= 448
       qr[kk] = w;
     }
+  } else {
+    // an idle score wave (fewer than 64 heads) keeps its probability rows at zero
+    for (int i = lane; i < 2 * 4 * 16 * (kPRow / 16); i += 64) {
+      const int seg = i % (kPRow / 16), r = (i / (kPRow / 16)) % 16, tb = i / (16 * (kPRow / 16));
+      *reinterpret_cast<i32x4*>(sh.pbuf + tb * kPTile + (16 * sw + r) * kPRow + 16 * seg) = i32x4{0, 0, 0, 0};
+    }
   }
 
-  // ---- compact this split's slot entries (valid = within [0, num_slots))
-  const int e0 = split * p.entries_per_split;
-  const int e1 = min(p.K, e0 + p.entries_per_split);
-  const int32_t* srow = p.slots + (int64_t)row * p.slots_ld;
-  int total = 0;
-  for (int base = e0; base < e1; base += NT * 8) {
-    int vals[8];
-    int wcount = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = base + i * NT + tid;
-      const int v = e < e1 ? srow[e] : -1;
-      const bool ok = v >= 0 && (int64_t)v < p.num_slots;
-      vals[i] = ok ? v : -1;
-      wcount += __popcll(__ballot(ok));
-    }
-    if (lane == 0) wave_cnt[wave] = wcount;
-    __syncthreads();
-    int off = total, all = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int c = wave_cnt[w];
-      off += w < wave ? c : 0;
-      all += c;
-    }
-    const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = vals[i] >= 0;
-      const unsigned long long b = __ballot(ok);
-      if (ok) clist[off + __popcll(b & below)] = vals[i];
-      off += __popcll(b);
-    }
-    total += all;
-    __syncthreads();
-  }
-
-  // ---- state: O^T accumulators o[db][hg] = dims wave*DPW + 32db + 8(r/4) + 4hh + r%4, head h_lo + 32hg + h32
-  f32x16 o[NDB][NW];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int hg = 0; hg < NW; ++hg) o[db][hg] = f32x16{};
-  float m_ref = -INFINITY;  // reference max of head qhead (log2 units), same in lanes h32 and h32+32
-  float m_max = -INFINITY;  // exact running max of head qhead
-  float l_run = 0.0f;       // this lane's share of the softmax sum of head qhead
-
-  const float sl_lat = p.scale_log2 * qexp_inv;
-
-  const int ntiles = (total + TT - 1) / TT;
+  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.0f;  // per head, same in its four lanes
   for (int pass = 0; pass < 2; ++pass) {
-  bool over = false;  // a score exceeded the reference by more than the headroom
-  if (ntiles > 0) issue_tile<NW, TT>(stage0, p.kv + (int64_t)clist[min(lane, total - 1)] * kRecordBytes, wave, lane);
-  for (int it = 0; it < ntiles; ++it) {
-    uint8_t* tile = (it & 1) ? stage1 : stage0;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile `it`
-    __syncthreads();  // tile `it` in LDS; every wave is done with tile it-1 (its probabilities included)
-    if (it + 1 < ntiles) {
-      const int idx = min((it + 1) * TT + lane, total - 1);
-      issue_tile<NW, TT>((it & 1) ? stage0 : stage1, p.kv + (int64_t)clist[idx] * kRecordBytes, wave, lane);
-    }
-    // scale chunk (chunk 32) is [record][4 fp32]; transpose it to [tile][record]
-    for (int i = tid; i < 4 * TT; i += NT) {
-      const int tok = i >> 2, t = i & 3;
-      sct[t * TT + tok] = *reinterpret_cast<const float*>(tile + 32 * CS + 16 * tok + 4 * t);
-    }
-    __syncthreads();
-    const int nin = min(TT, total - it * TT);
-
-    // ---- per 32-token block: scores of this wave's 32 heads, softmax numerators, P'
-    // s[r] <-> token 32b + 8(r/4) + 4hh + r%4 of the tile; lane = head qhead
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));  // recompute lane-derived addresses here instead of hoisting them
-    const int l32 = lane_o & 31, lhh = lane_o >> 5;
+    bool over = false;  // a score exceeded the reference by more than the headroom
+    for (int n = 0; n <= bk.ntiles; ++n) {
+      __syncthreads();  // tile n staged; P'(n-2) consumed by the value waves
+      if (!active || n >= bk.ntiles) continue;
+      // ---- S^T for tile n: lane holds head hl, tokens 16hf + 4g + r
+      const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
+      const int nin = min(kTT, bk.total - n * kTT);
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));  // recompute lane-derived addresses here instead of hoisting them
+      const int tok_a = lane_o & 15;   // record operand row of this lane
+      const int go = lane_o >> 4;
+      f32x4 s[2];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (32 * b >= nin) break;
-      const uint8_t* krow = tile + 16 * (32 * b + l32);
-      // rope dims 16kk + 8hh .. +7 (bf16, both operands scaled by 2^e_h): chunk 33 + 2kk + hh
-      f32x16 s = {};
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint8_t* kr = tile + 16 * (16 * hf + tok_a);
+        f32x4 acc = {};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(krow + (33 + 2 * kk + lhh) * CS), qr[kk], s);
+        for (int kk = 0; kk < 2; ++kk)
+          acc = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + (kRopeChunk + 4 * kk + go) * kCS), qr[kk], acc);
+        s[hf] = acc;
+      }
+      f32x4 sc[2][4];  // [hf][r]: the four tile scales of token 16hf + 4g + r
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x16 acc = {};
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int c0 = 8 * t + 4 * kk + 2 * lhh;  // dims 128t + 64kk + 32hh .. +31
-          const i32x4 a0 = *reinterpret_cast<const i32x4*>(krow + c0 * CS);
-          const i32x4 a1 = *reinterpret_cast<const i32x4*>(krow + (c0 + 1) * CS);
+        for (int r = 0; r < 4; ++r)
+          sc[hf][r] = *reinterpret_cast<const f32x4*>(tile + kScaleChunk * kCS + 16 * (16 * hf + 4 * go + r));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint8_t* kr = tile + 16 * (16 * hf + tok_a) + (8 * t + 2 * go) * kCS;
+          const i32x4 a0 = *reinterpret_cast<const i32x4*>(kr);
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(kr + kCS);
           const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          acc = mfma_fp8(a, qh[t][kk], acc);
-          acc = mfma_fp8(a, ql[t][kk], acc);
+          f32x4 acc = mfma16_fp8(a, qh[t], f32x4{});
+          acc = mfma16_fp8(a, ql[t], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[hf][r] += sc[hf][r][t] * acc[r];
         }
+      float pv[8];
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + t * TT + 32 * b + 8 * qd + 4 * lhh);
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[4 * qd + i] += sc[i] * acc[4 * qd + i];
+        for (int r = 0; r < 4; ++r) {
+          const float v = s[hf][r] * cq;
+          pv[4 * hf + r] = 16 * hf + 4 * go + r < nin ? v : -INFINITY;
         }
-      }
-      s *= sl_lat;
-      if (nin - 32 * b < 32) {
+      float mx = pv[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + 4 * lhh + (r & 3) >= nin - 32 * b) s[r] = -INFINITY;
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, pv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       m_max = fmaxf(m_max, mx);
       if (m_ref == -INFINITY) m_ref = mx;
       over |= mx > m_ref + kRefHeadroom;
-      const float mref = m_ref == -INFINITY ? 0.0f : m_ref;
       float lsum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = fast_exp2(s[r] - mref);
-        lsum += s[r];
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = fast_exp2(pv[i] - m_ref);
+        lsum += pv[i];
       }
       l_run += lsum;
-      // P'_t = bf16(p * scale(token, t)) as [t][head][token]; granule tok/8 = 4b + qd, byte 8hh inside it
-      const int ph = wave * 32 + l32;
-      uint8_t* prow = pbuf + ph * PS + 8 * lhh;
+      // P'_t = bf16(p * scale(token, t)) as [t][head][token]; 16-byte granule k of a head row
+      // is stored at granule k ^ ((head >> 2) & 3)
+      const int hw = 16 * sw + tok_a;
+      uint8_t* pw = sh.pbuf + (n & 1) * kPBuf + hw * kPRow + 8 * (go & 1);
+      const int swz = (hw >> 2) & 3;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + t * TT + 32 * b + 8 * qd + 4 * lhh);
-          const bf16x4 v = {(__bf16)(s[4 * qd] * sc[0]), (__bf16)(s[4 * qd + 1] * sc[1]),
-                            (__bf16)(s[4 * qd + 2] * sc[2]), (__bf16)(s[4 * qd + 3] * sc[3])};
-          *reinterpret_cast<bf16x4*>(prow + t * PT + 16 * ((4 * b + qd) ^ (ph & GM))) = v;
+        for (int hf = 0; hf < 2; ++hf) {
+          const bf16x4 v = {(__bf16)(pv[4 * hf] * sc[hf][0][t]), (__bf16)(pv[4 * hf + 1] * sc[hf][1][t]),
+                            (__bf16)(pv[4 * hf + 2] * sc[hf][2][t]), (__bf16)(pv[4 * hf + 3] * sc[hf][3][t])};
+          *reinterpret_cast<bf16x4*>(pw + t * kPTile + 16 * ((2 * hf + (go >> 1)) ^ swz)) = v;
         }
     }
-    __syncthreads();
+    // a second pass, with the exact max as reference, only if some score outgrew the headroom
+    if (!__syncthreads_or(over)) break;
+    m_ref = m_max;
+    l_run = 0.0f;
+  }
 
-    // ---- O^T += V^T P'^T for this wave's dims and every head of the workgroup
-#pragma unroll
-    for (int ks = 0; ks < TT / 16; ++ks) {
-      if (16 * ks < nin) {
-        bf16x8 bq[TPW][NW];
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-          for (int hg = 0; hg < NW; ++hg)
-            bq[tt][hg] = *reinterpret_cast<const bf16x8*>(pbuf + (wave * TPW + tt) * PT + (32 * hg + l32) * PS +
-                                                          16 * ((2 * ks + lhh) ^ ((32 * hg + l32) & GM)));
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int mbg = wave * NDB + db;  // global 32-dim block: chunks 2mbg, 2mbg+1
-          const int vrow = 16 * (8 * ((lane_o >> 4) >> 1) + ((lane_o & 15) >> 1)) + 8 * (lane_o & 1) +
-                           ((lane_o >> 4) & 1) * CS;  // tr8 row of this lane
-          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (SMLA_LDS i32x2*)(tile + 2 * mbg * CS + 16 * 16 * ks + vrow));
-          const bf16x8 va = widen_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
-          const int tt = db / 4;  // 4 dim blocks per scale tile
-#pragma unroll
-          for (int hg = 0; hg < NW; ++hg) o[db][hg] = mfma_bf16(va, bq[tt][hg], o[db][hg]);
-        }
+  // ---- per-head (max, sum) for the value waves; lse or the split partial
+  if (active) {
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const float mo = l_tot > 0.0f ? m_ref : -INFINITY;
+    if (g == 0) {
+      sh.ml[2 * hl] = mo;
+      sh.ml[2 * hl + 1] = l_tot;
+      const int head = bk.h_lo + hl;
+      if (p.splits == 1) {
+        p.lse[(int64_t)bk.row * p.l_st + (int64_t)head * p.l_sh] =
+            l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t pidx = ((int64_t)bk.row * p.splits + bk.split) * p.H + head;
+        p.ws_ml[pidx * 2 + 0] = mo;
+        p.ws_ml[pidx * 2 + 1] = l_tot;
       }
     }
   }
+  __syncthreads();  // sums visible to the value waves
+}
 
-  // a second pass, with the exact max as reference, only if some score outgrew the headroom
-  if (!__syncthreads_or(over)) break;
-  m_ref = m_max;
-  l_run = 0.0f;
+// ---------------------------------------------------------------------------------------
+// Value wave `vw` (0..3): output dims 128vw .. +127 (scale tile vw) of every head of the
+// block; also the loader of the tiles.
+__device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, const Block& bk, int vw, int lane) {
+  const int nhg = (bk.nh + 31) >> 5;  // 32-head groups
+  // O^T blocks o[db][hg]: dims 128vw + 32db + 8(r/4) + 4(lane/32) + r%4, head 32hg + lane%32
+  f32x16 o[4][2];
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int hg = 0; hg < NW; ++hg) o[db][hg] = f32x16{};
-  }  // pass
-
-  // ---- epilogue: per-head sums from the score waves, normalisation by the value waves
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  __syncthreads();  // every wave is done reading pbuf
-  if (hh == 0) linv_s[wave * 32 + h32] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (p.splits == 1 && q_ok && hh == 0)
-    p.lse[(int64_t)row * p.l_st + (int64_t)qhead * p.l_sh] =
-        l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (p.splits > 1 && q_ok && hh == 0) {
-    const int64_t pidx = ((int64_t)row * p.splits + split) * p.H + qhead;
-    p.ws_ml[pidx * 2 + 0] = l_tot > 0.0f ? m_ref : -INFINITY;
-    p.ws_ml[pidx * 2 + 1] = l_tot;
+      for (int hg = 0; hg < 2; ++hg) o[db][hg] = f32x16{};
+    for (int n = 0; n < kAhead && n < bk.ntiles; ++n)
+      issue_tile(sh.stage + n * kTileBytes, lane_record(p, sh, n, bk.total, lane), vw, lane);
+    for (int n = 0; n <= bk.ntiles; ++n) {
+      wait_tile(min(kAhead - 1, max(bk.ntiles - 1 - n, 0)), vw);  // tile n is in
+      __syncthreads();  // tile n staged; P'(n-1) written; tile n-2 and P'(n-2) consumed
+      if (n + kAhead < bk.ntiles)
+        issue_tile(sh.stage + ((n + kAhead) % kStages) * kTileBytes, lane_record(p, sh, n + kAhead, bk.total, lane),
+                   vw, lane);
+      if (n == 0) continue;
+      // ---- O^T += V^T P'^T for tile n-1
+      const int m = n - 1;
+      const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
+      const uint8_t* pb = sh.pbuf + (m & 1) * kPBuf + vw * kPTile;
+      const int nin = min(kTT, bk.total - m * kTT);
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int h32 = lane_o & 31, lh = lane_o >> 5;
+      // tr8 row of this lane: record 8(lane/32) + (lane%16)/2, 8-byte half lane&1, chunk (lane/16)&1
+      const int vrow = 16 * (8 * lh + ((lane_o & 15) >> 1)) + 8 * (lane_o & 1) + ((lane_o >> 4) & 1) * kCS;
+#pragma unroll
+      for (int ks = 0; ks < kTT / 16; ++ks) {
+        if (16 * ks >= nin) break;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int hg = 0; hg < 2; ++hg) {
+          const int hl = 32 * hg + h32;
+          pf[hg] = *reinterpret_cast<const bf16x8*>(pb + hl * kPRow + 16 * ((2 * ks + lh) ^ ((hl >> 2) & 3)));
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int cb = 4 * vw + db;  // global 32-dim block: chunks 2cb, 2cb + 1
+          const i32x2 raw =
+              __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS i32x2*)(tile + 2 * cb * kCS + 256 * ks + vrow));
+          const bf16x8 va = widen_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
+          o[db][0] = mfma32_bf16(va, pf[0], o[db][0]);
+          if (nhg > 1) o[db][1] = mfma32_bf16(va, pf[1], o[db][1]);
+        }
+      }
+    }
+    if (!__syncthreads_or(false)) break;
   }
-  __syncthreads();
-  const int dbase = wave * DPW + 4 * hh;  // + 32db + 8qd
-  if (p.splits == 1) {
+  __syncthreads();  // the score waves' (max, sum) are in LDS
+
+  const int h32 = lane & 31;
+  const int dbase = 128 * vw + 4 * (lane >> 5);  // + 32db + 8qd
 #pragma unroll
-    for (int hg = 0; hg < NW; ++hg) {
-      const int head = h_lo + 32 * hg + h32;
-      if (head >= p.H) continue;
-      const float inv = linv_s[32 * hg + h32];
+  for (int hg = 0; hg < 2; ++hg) {
+    const int hl = 32 * hg + h32;
+    if (hl >= bk.nh) continue;
+    const int head = bk.h_lo + hl;
+    if (p.splits == 1) {
+      const float lt = sh.ml[2 * hl + 1];
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
       if (p.out_fp32) {
-        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)row * p.o_st + (int64_t)head * p.o_sh + dbase;
+        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd)
             *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd) =
                 f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
       } else {
-        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)row * p.o_st + (int64_t)head * p.o_sh + dbase;
+        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd)
             *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * qd) =
                 bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
                        (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
       }
+    } else {
+      // split-K: this split's unnormalised partial
+      float* po = p.ws_o + (((int64_t)bk.row * p.splits + bk.split) * p.H + head) * kLatent + dbase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd) =
+              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]};
     }
-    return;
   }
+}
 
-  // ---- split-K: publish this split's unnormalised partial, the last arrival combines
-#pragma unroll
-  for (int hg = 0; hg < NW; ++hg) {
-    const int head = h_lo + 32 * hg + h32;
-    if (head >= p.H) continue;
-    float* po = p.ws_o + (((int64_t)row * p.splits + split) * p.H + head) * kLatent + dbase;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd) =
-            f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]};
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.ws_cnt + (int64_t)row * p.head_blocks + hb, 1, __ATOMIC_ACQ_REL,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = old == p.splits - 1;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-
-  const int nh = min(HPB, p.H - h_lo);
-  for (int item = tid; item < nh * (kLatent / 4); item += NT) {
+// The last split of a (row, head block) to arrive merges every split's partial.
+__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, int tid) {
+  for (int item = tid; item < bk.nh * (kLatent / 4); item += kThreads) {
     const int hrel = item / (kLatent / 4);
     const int d4 = item - hrel * (kLatent / 4);
-    const int h = h_lo + hrel;
-    const float* ml = p.ws_ml + ((int64_t)row * p.splits * p.H + h) * 2;  // split sp at + sp * H * 2
+    const int h = bk.h_lo + hrel;
+    const float* ml = p.ws_ml + ((int64_t)bk.row * p.splits * p.H + h) * 2;  // split sp at + sp * H * 2
     float M = -INFINITY;
     for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -463,21 +459,101 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_kernel(DecodeParams p) {
         if (ms == -INFINITY) continue;
         const float w = fast_exp2(ms - M);
         L += w * __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2 + 1);
-        const int64_t pidx = ((int64_t)row * p.splits + sp) * p.H + h;
+        const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + h;
         acc += w * __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
       }
     }
     const bool empty = !(L > 0.0f);
     acc *= empty ? 0.0f : 1.0f / L;
     if (p.out_fp32) {
-      float* orow = reinterpret_cast<float*>(p.out) + (int64_t)row * p.o_st + (int64_t)h * p.o_sh;
+      float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
       *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc;
     } else {
-      __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)row * p.o_st + (int64_t)h * p.o_sh;
+      __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
       *reinterpret_cast<bf16x4*>(orow + 4 * d4) = bf16x4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
     }
-    if (d4 == 0) p.lse[(int64_t)row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
+    if (d4 == 0) p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
   }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) Shared sh;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+  const int lane = tid & 63;
+
+  // Consecutive blocks are dispatched round-robin over the 8 XCDs; give every XCD a
+  // contiguous range of work items so the head blocks and splits of a row run side by side
+  // on one XCD and share its L2.
+  const int per_xcd = (int)((gridDim.x + 7) / 8);
+  const int wg = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (wg >= p.T * p.head_blocks * p.splits) return;
+  Block bk;
+  bk.split = wg % p.splits;
+  const int rest = wg / p.splits;
+  bk.hb = rest % p.head_blocks;
+  bk.row = rest / p.head_blocks;
+  bk.h_lo = bk.hb * kHB;
+  bk.nh = min(kHB, p.H - bk.h_lo);  // a multiple of 16
+
+  // ---- compact this split's slot entries (valid = within [0, num_slots))
+  const int e0 = bk.split * p.entries_per_split;
+  const int e1 = min(p.K, e0 + p.entries_per_split);
+  const int32_t* srow = p.slots + (int64_t)bk.row * p.slots_ld;
+  int total = 0;
+  for (int base = e0; base < e1; base += kThreads * 4) {
+    int vals[4];
+    int wcount = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = base + i * kThreads + tid;
+      const int v = e < e1 ? srow[e] : -1;
+      const bool ok = v >= 0 && (int64_t)v < p.num_slots;
+      vals[i] = ok ? v : -1;
+      wcount += __popcll(__ballot(ok));
+    }
+    if (lane == 0) sh.wave_cnt[wave] = wcount;
+    __syncthreads();
+    int off = total, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int c = sh.wave_cnt[w];
+      off += w < wave ? c : 0;
+      all += c;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = vals[i] >= 0;
+      const unsigned long long bm = __ballot(ok);
+      if (ok) sh.clist[off + __popcll(bm & below)] = vals[i];
+      off += __popcll(bm);
+    }
+    total += all;
+    __syncthreads();
+  }
+  bk.total = total;
+  bk.ntiles = (total + kTT - 1) / kTT;
+
+  // The two roles run the same number of workgroup barriers, one per loop step.
+  if (wave < 4)
+    score_role(p, sh, bk, wave, lane);
+  else
+    value_role(p, sh, bk, wave - 4, lane);
+  if (p.splits == 1) return;
+
+  // ---- split-K: the last split of this (row, head block) to arrive combines all of them
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.ws_cnt + (int64_t)bk.row * p.head_blocks + bk.hb, 1, __ATOMIC_ACQ_REL,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    sh.last_flag = old == p.splits - 1;
+  }
+  __syncthreads();
+  if (!sh.last_flag) return;
+  __threadfence();
+  combine_splits(p, bk, tid);
 }
 
 __global__ void zero_counters(int32_t* cnt, int64_t n) {
@@ -496,19 +572,7 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStrea
     const int64_t n = (int64_t)p.T * plan.head_blocks;
     hipLaunchKernelGGL(zero_counters, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.ws_cnt, n);
   }
-  switch (plan.waves) {
-    case 1:
-      hipLaunchKernelGGL((decode_kernel<1, 32>), dim3(grid), dim3(64), 0, stream, p);
-      break;
-    case 2:
-      hipLaunchKernelGGL((decode_kernel<2, 32>), dim3(grid), dim3(128), 0, stream, p);
-      break;
-    case 4:
-      hipLaunchKernelGGL((decode_kernel<4, 64>), dim3(grid), dim3(256), 0, stream, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

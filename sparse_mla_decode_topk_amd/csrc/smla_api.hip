@@ -29,21 +29,19 @@ int device_cus() {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split plan for a decode call.  A workgroup holds one wave per SIMD, 32 heads per wave
-// (1, 2 or 4 waves: up to 128 heads of one row); with 4 waves its LDS footprint allows one
-// workgroup per CU, with 1 or 2 waves two.  Rows are cut into top-k ranges only when rows
-// cannot cover every workgroup slot of the device.
+// Split plan for a decode call.  A workgroup covers up to 64 heads of one row (8 waves, two
+// per SIMD) and its LDS footprint allows one workgroup per CU.  Rows are cut into top-k
+// ranges only when (row, head block) pairs cannot cover every CU of the device.
 DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cus) {
   DecodePlan pl{};
-  pl.waves = H <= 32 ? 1 : (H <= 64 ? 2 : 4);
-  pl.head_blocks = 1;
+  pl.head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const int min_splits = K > 0 ? (K + kMaxEntriesPerSplit - 1) / kMaxEntriesPerSplit : 1;
   int splits;
   if (num_splits > 0) {
     splits = num_splits;
   } else {
     const int64_t wgs = (int64_t)T * pl.head_blocks;
-    const int64_t slots = (int64_t)cus * (pl.waves == 4 ? 1 : 2);
+    const int64_t slots = (int64_t)cus;
     splits = 1;
     if (wgs > 0 && wgs < slots) {
       const int64_t want = (slots + wgs - 1) / wgs;
@@ -175,7 +173,7 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
   p.splits = plan.splits;
   p.entries_per_split = plan.entries_per_split;
   p.head_blocks = plan.head_blocks;
-  p.heads_per_block = plan.waves * kHeadsPerWave;
+  p.heads_per_block = kHeadsPerBlock;
   if (plan.ws_total > 0) {
     char* ws = static_cast<char*>(workspace);
     p.ws_cnt = reinterpret_cast<int32_t*>(ws);

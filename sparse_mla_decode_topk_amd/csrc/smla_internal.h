@@ -14,7 +14,7 @@ constexpr int kScaleOffset = 512;
 constexpr int kRopeOffset = 528;
 constexpr int kMaxEntriesPerSplit = 2048;  // slot entries one decode workgroup compacts
 constexpr int kMaxSplits = 64;
-constexpr int kHeadsPerWave = 32;
+constexpr int kHeadsPerBlock = 64;           // heads one decode workgroup covers
 
 struct ConvertParams {
   const int32_t* ids;
@@ -64,7 +64,6 @@ struct MergeParams {
 };
 
 struct DecodePlan {
-  int32_t waves;        // waves per workgroup (32 heads each)
   int32_t head_blocks;  // workgroups per row along heads
   int32_t splits;       // top-k ranges per row
   int32_t entries_per_split;
