@@ -126,6 +126,19 @@ __device__ __forceinline__ void split_e4m3(float x0, float x1, float x2, float x
   lo = l;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global memory, which
+// makes every wave drain its in-flight HBM -> LDS copies at each barrier; the copies are
+// instead waited for explicitly (wait_tile) by the waves that issued them.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// max of a value over lanes l, l^16, l^32, l^48 (every lane gets it), on the VALU
+__device__ __forceinline__ float max4x16(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -147,6 +160,17 @@ __device__ __forceinline__ void wait_tile(int tiles_newer, int b) {
   }
 }
 
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes land at
+// LDS address lds + 16 i.  Issued as inline assembly so the compiler does not treat every
+// later LDS read as a possible alias of the copy and drain all copies in flight before it;
+// the waves wait for their own copies explicitly (wait_tile) before the barrier that
+// publishes a tile.  M0 (the LDS base of the copy) is written right before each copy; the
+// kernel has no other M0 user.
+__device__ __forceinline__ void lds_dma16(const uint8_t* src, const uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(SMLA_LDS void*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+}
+
 // HBM -> LDS copy of one tile by value wave b (0..3): load j moves chunks 2j and 2j+1 of all
 // 32 records (lane r < 32: chunk 2j of record r, lane 32 + r: chunk 2j + 1 of record r), so
 // its LDS destination is the contiguous kilobyte j of the tile.  `rec` is this lane's record
@@ -155,8 +179,7 @@ __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, i
 #pragma unroll
   for (int k = 0; k < (kLoads + 3) / 4; ++k) {
     const int j = b + 4 * k;
-    if (j < kLoads - 1 || (j == kLoads - 1 && lane < 32))
-      __builtin_amdgcn_global_load_lds(rec + 32 * j, (SMLA_LDS void*)(stage + 1024 * j), 16, 0, 0);
+    if (j < kLoads - 1 || (j == kLoads - 1 && lane < 32)) lds_dma16(rec + 32 * j, stage + 1024 * j);
   }
 }
 
@@ -243,7 +266,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
   for (int pass = 0; pass < 2; ++pass) {
     bool over = false;  // a score exceeded the reference by more than the headroom
     for (int n = 0; n <= bk.ntiles; ++n) {
-      __syncthreads();  // tile n staged; P'(n-2) consumed by the value waves
+      lds_barrier();  // tile n staged; P'(n-2) consumed by the value waves
       if (!active || n >= bk.ntiles) continue;
       // ---- S^T for tile n: lane holds head hl, tokens 16hf + 4g + r
       const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
@@ -285,17 +308,18 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = s[hf][r] * cq;
-          pv[4 * hf + r] = 16 * hf + 4 * go + r < nin ? v : -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) pv[4 * hf + r] = s[hf][r] * cq;
+      if (nin < kTT) {  // tail tile: entries past the end of the list get p = 0
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (16 * (i >> 2) + 4 * go + (i & 3) >= nin) pv[i] = -INFINITY;
+      }
       float mx = pv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, pv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max4x16(mx);
       m_max = fmaxf(m_max, mx);
-      if (m_ref == -INFINITY) m_ref = mx;
+      m_ref = m_ref == -INFINITY ? mx : m_ref;
       over |= mx > m_ref + kRefHeadroom;
       float lsum = 0.0f;
 #pragma unroll
@@ -350,7 +374,6 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 // Value wave `vw` (0..3): output dims 128vw .. +127 (scale tile vw) of every head of the
 // block; also the loader of the tiles.
 __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, const Block& bk, int vw, int lane) {
-  const int nhg = (bk.nh + 31) >> 5;  // 32-head groups
   // O^T blocks o[db][hg]: dims 128vw + 32db + 8(r/4) + 4(lane/32) + r%4, head 32hg + lane%32
   f32x16 o[4][2];
   for (int pass = 0; pass < 2; ++pass) {
@@ -362,7 +385,7 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       issue_tile(sh.stage + n * kTileBytes, lane_record(p, sh, n, bk.total, lane), vw, lane);
     for (int n = 0; n <= bk.ntiles; ++n) {
       wait_tile(min(kAhead - 1, max(bk.ntiles - 1 - n, 0)), vw);  // tile n is in
-      __syncthreads();  // tile n staged; P'(n-1) written; tile n-2 and P'(n-2) consumed
+      lds_barrier();  // tile n staged; P'(n-1) written; tile n-2 and P'(n-2) consumed
       if (n + kAhead < bk.ntiles)
         issue_tile(sh.stage + ((n + kAhead) % kStages) * kTileBytes, lane_record(p, sh, n + kAhead, bk.total, lane),
                    vw, lane);
@@ -371,31 +394,34 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       const int m = n - 1;
       const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
       const uint8_t* pb = sh.pbuf + (m & 1) * kPBuf + vw * kPTile;
-      const int nin = min(kTT, bk.total - m * kTT);
       int lane_o = lane;
       asm volatile("" : "+v"(lane_o));
       const int h32 = lane_o & 31, lh = lane_o >> 5;
       // tr8 row of this lane: record 8(lane/32) + (lane%16)/2, 8-byte half lane&1, chunk (lane/16)&1
       const int vrow = 16 * (8 * lh + ((lane_o & 15) >> 1)) + 8 * (lane_o & 1) + ((lane_o >> 4) & 1) * kCS;
+      // all operands of the tile first (tokens past the end carry P' = 0 against real records)
+      bf16x8 pf[2][2], va[2][4];
 #pragma unroll
       for (int ks = 0; ks < kTT / 16; ++ks) {
-        if (16 * ks >= nin) break;
-        bf16x8 pf[2];
 #pragma unroll
         for (int hg = 0; hg < 2; ++hg) {
           const int hl = 32 * hg + h32;
-          pf[hg] = *reinterpret_cast<const bf16x8*>(pb + hl * kPRow + 16 * ((2 * ks + lh) ^ ((hl >> 2) & 3)));
+          pf[ks][hg] = *reinterpret_cast<const bf16x8*>(pb + hl * kPRow + 16 * ((2 * ks + lh) ^ ((hl >> 2) & 3)));
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int cb = 4 * vw + db;  // global 32-dim block: chunks 2cb, 2cb + 1
           const i32x2 raw =
               __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS i32x2*)(tile + 2 * cb * kCS + 256 * ks + vrow));
-          const bf16x8 va = widen_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
-          o[db][0] = mfma32_bf16(va, pf[0], o[db][0]);
-          if (nhg > 1) o[db][1] = mfma32_bf16(va, pf[1], o[db][1]);
+          va[ks][db] = widen_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
         }
       }
+#pragma unroll
+      for (int ks = 0; ks < kTT / 16; ++ks)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int hg = 0; hg < 2; ++hg) o[db][hg] = mfma32_bf16(va[ks][db], pf[ks][hg], o[db][hg]);
     }
     if (!__syncthreads_or(false)) break;
   }
