@@ -53,8 +53,8 @@ def roofline_entry(byts, flops, seconds):
 
 
 def cpu_baseline(w, budget_s):
-    """fp64 oracle of the same DCP2 step (converts, shard attention, merge) on the first rows
-    until the time budget is spent; rows/s over the rows done."""
+    """fp64 oracle of the same DCP2 step (converts, shard attention, merge) over the rows in
+    order, wrapping around, until the time budget is spent; rows/s over the rows done."""
     import numpy as np
     import oracle.smla_oracle as O
     try:
@@ -64,8 +64,9 @@ def cpu_baseline(w, budget_s):
         threads = os.cpu_count() or 1
     rows_done, t0 = 0, time.perf_counter()
     chunk = 4
-    while rows_done < w.T and time.perf_counter() - t0 < budget_s:
-        rows = list(range(rows_done, min(w.T, rows_done + chunk)))
+    while time.perf_counter() - t0 < budget_s:
+        start = rows_done % w.T
+        rows = list(range(start, min(w.T, start + chunk)))
         sub = w.rows(rows)
         q = sub.q_f32()
         outs, lses = [], []
@@ -78,14 +79,16 @@ def cpu_baseline(w, budget_s):
         rows_done += len(rows)
     dt = time.perf_counter() - t0
     return {"value": round(rows_done / dt, 3), "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows_done} of {w.T} rows of the same DCP2 step (fp64 numpy oracle: 2 shard converts, "
-                      f"shard attention, LSE merge), {dt:.1f} s on {os.cpu_count()} host CPUs"}
+            "sample": f"{rows_done} rows (the {w.T} rows of the same DCP2 step in order, wrapping) through the fp64 "
+                      f"numpy oracle: 2 shard converts, shard attention, LSE merge; {dt:.1f} s on "
+                      f"{os.cpu_count()} host CPUs"}
 
 
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": None, "fetch_bytes": None, "write_bytes": None}
+DECODE_TRAFFIC = {"sources_sha256": "5aab9d6919f40e94083c3b42a25e3293df98eedaba59a985f62aa4c548d201f1",
+                  "fetch_bytes": 227335168, "write_bytes": 67244032}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
 

@@ -18,7 +18,7 @@ What it follows (the three pages this project is built from):
   (vllm-project/vllm pull request 55879), "Root causes and fixes", subsection
   "Zero-local-sequence DCP warmup rank" (a shard with no local rows emits -inf LSE).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
 
 * R1 record layout: 656 bytes = 512 e4m3fn codes, 4 fp32 LE scales (scale i for
   latent dims 128i..128i+127), 64 bf16 LE rope values.  The pages give only the
