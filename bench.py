@@ -87,8 +87,8 @@ def cpu_baseline(w, budget_s):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "5aab9d6919f40e94083c3b42a25e3293df98eedaba59a985f62aa4c548d201f1",
-                  "fetch_bytes": 227335168, "write_bytes": 67244032}
+DECODE_TRAFFIC = {"sources_sha256": "102c27ab85ec5cac774037c7f5253ca54708e2167fd5ce8d88b5b4fb240b94a2",
+                  "fetch_bytes": 227313802, "write_bytes": 67246144}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
 

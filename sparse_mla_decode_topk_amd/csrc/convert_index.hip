@@ -7,8 +7,11 @@
 // FlashInfer sparse MLA", "Summary": the per-row valid counts are produced alongside.
 //
 // One workgroup per row; consecutive lanes take consecutive entries (coalesced int32
-// traffic), the row's valid count is a workgroup reduction, so no atomics and no pre-zeroed
-// output are needed.
+// traffic).  Each thread handles kPer entries per pass with all of their id loads in flight
+// together, then all of their block-table loads, so a row costs two dependent memory round
+// trips instead of two per entry.  Power-of-two block size, DCP size and interleave (the
+// usual case) take shifts and masks instead of integer division.  The row's valid count is
+// a workgroup reduction, so no atomics and no pre-zeroed output are needed.
 
 #include "smla_internal.h"
 
@@ -16,6 +19,11 @@ namespace smla {
 namespace {
 
 constexpr int kConvThreads = 256;
+constexpr int kPer = 8;  // entries per thread per pass
+
+// x / d and x % d for x >= 0, d >= 1; `lg` is log2(d) when d is a power of two, else -1.
+__device__ __forceinline__ int div_pos(int x, int d, int lg) { return lg >= 0 ? x >> lg : x / d; }
+__device__ __forceinline__ int mod_pos(int x, int d, int lg) { return lg >= 0 ? x & (d - 1) : x % d; }
 
 __global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) {
   __shared__ int wsum[kConvThreads / 64];
@@ -28,34 +36,52 @@ __global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) 
   const int32_t* btrow = p.bt + (int64_t)(req_ok ? b : 0) * p.bt_ld;
   const int D = p.dcp_size, I = p.interleave, r = p.dcp_rank, B = p.block_size;
   int count = 0;
-  for (int j = tid; j < p.K; j += kConvThreads) {
-    const int id = ids[j];
-    int slot = -1;
-    if (id >= 0 && req_ok) {
-      bool own = true;
-      int pos = id;
-      if (D > 1) {
-        const int g = id / I;
-        own = (g % D) == r;
-        pos = (g / D) * I + (id - g * I);
-      }
-      if (own) {
-        const int blk = pos / B;
-        if (blk < p.bt_width) {
-          const int phys = btrow[blk];
-          if (phys >= 0) {
-            const int64_t s = (int64_t)phys * B + (pos - blk * B);
-            slot = s <= 0x7fffffffLL ? (int)s : -1;
-          }
+  for (int base = 0; base < p.K; base += kConvThreads * kPer) {
+    int id[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = base + i * kConvThreads + tid;
+      id[i] = j < p.K ? ids[j] : -1;
+    }
+    int blk[kPer], off[kPer];  // block-table column and offset in the block; blk = -1: no slot
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      blk[i] = -1;
+      off[i] = 0;
+      const int x = id[i];
+      if (x >= 0 && req_ok) {
+        bool own = true;
+        int pos = x;
+        if (D > 1) {
+          const int g = div_pos(x, I, p.lg_interleave);
+          own = mod_pos(g, D, p.lg_dcp) == r;
+          pos = div_pos(g, D, p.lg_dcp) * I + (x - g * I);
+        }
+        const int bi = div_pos(pos, B, p.lg_block);
+        if (own && bi < p.bt_width) {
+          blk[i] = bi;
+          off[i] = pos - bi * B;
         }
       }
     }
-    out[j] = slot;
-    count += slot >= 0;
+    int phys[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) phys[i] = blk[i] >= 0 ? btrow[blk[i]] : -1;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = base + i * kConvThreads + tid;
+      int slot = -1;
+      if (phys[i] >= 0) {
+        const int64_t s = (int64_t)phys[i] * B + off[i];
+        slot = s <= 0x7fffffffLL ? (int)s : -1;
+      }
+      if (j < p.K) out[j] = slot;
+      count += slot >= 0;
+    }
   }
   if (p.valid == nullptr) return;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) count += __shfl_xor(count, off);
+  for (int o = 32; o > 0; o >>= 1) count += __shfl_xor(count, o);
   if ((tid & 63) == 0) wsum[tid >> 6] = count;
   __syncthreads();
   if (tid == 0) {
@@ -66,9 +92,20 @@ __global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) 
   }
 }
 
+int log2_exact(int v) {
+  if (v < 1 || (v & (v - 1)) != 0) return -1;
+  int lg = 0;
+  while ((1 << lg) < v) ++lg;
+  return lg;
+}
+
 }  // namespace
 
-hipError_t launch_convert(const ConvertParams& p, hipStream_t stream) {
+hipError_t launch_convert(const ConvertParams& p_in, hipStream_t stream) {
+  ConvertParams p = p_in;
+  p.lg_block = log2_exact(p.block_size);
+  p.lg_dcp = log2_exact(p.dcp_size);
+  p.lg_interleave = log2_exact(p.interleave);
   hipLaunchKernelGGL(convert_kernel, dim3(p.T), dim3(kConvThreads), 0, stream, p);
   return hipGetLastError();
 }

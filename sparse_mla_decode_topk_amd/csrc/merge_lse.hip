@@ -7,7 +7,8 @@
 //
 // HBM-bound: each (row, head) pair reads S partial rows of 512 values and writes one.  A
 // wave handles one (row, head) pair: the S weights are computed once per pair, every lane
-// moves 8 consecutive dims with 16- or 32-byte accesses.
+// moves 8 consecutive dims with 16- or 32-byte accesses.  Up to 8 shards the partial rows of
+// a pair are all in flight together.
 
 #include "smla_internal.h"
 
@@ -35,32 +36,8 @@ __device__ __forceinline__ void load8(const void* base, bool fp32, int64_t off, 
   }
 }
 
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
-  if (pair >= (int64_t)p.T * p.H) return;
-  const int t = (int)(pair / p.H);
-  const int h = (int)(pair - (int64_t)t * p.H);
-
-  // weights: every lane computes them for all S (S <= 64, values come from L1/L2)
-  float m = -INFINITY;
-  for (int s = 0; s < p.S; ++s) m = fmaxf(m, p.lparts[s * p.lp_ss + t * p.lp_st + h * p.lp_sh]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float lse = -INFINITY;
-  if (m != -INFINITY) {
-    float tot = 0.0f;
-    for (int s = 0; s < p.S; ++s) tot += exp2f((p.lparts[s * p.lp_ss + t * p.lp_st + h * p.lp_sh] - m) * kLog2e);
-    lse = m + logf(tot);
-    for (int s = 0; s < p.S; ++s) {
-      const float ls = p.lparts[s * p.lp_ss + t * p.lp_st + h * p.lp_sh];
-      if (ls == -INFINITY) continue;  // an empty partial contributes nothing
-      const float w = exp2f((ls - lse) * kLog2e);
-      float v[8];
-      load8(p.parts, p.part_fp32, s * p.p_ss + t * p.p_st + h * p.p_sh + 8 * lane, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
-    }
-  }
+__device__ __forceinline__ void store_out(const MergeParams& p, int t, int h, int lane, const float (&acc)[8],
+                                          float lse) {
   if (p.out_fp32) {
     f32x4* o = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + t * p.o_st + h * p.o_sh + 8 * lane);
     o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
@@ -74,12 +51,84 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
   if (p.lse != nullptr && lane == 0) p.lse[t * p.l_st + h * p.l_sh] = lse;
 }
 
+// SM > 0: S <= SM, and every partial LSE, then every partial row, is loaded in one batch so
+// a wave waits for two memory round trips in all.  SM == 0: any S, one partial at a time.
+template <int SM>
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (pair >= (int64_t)p.T * p.H) return;
+  const int t = (int)(pair / p.H);
+  const int h = (int)(pair - (int64_t)t * p.H);
+  const float* lrow = p.lparts + t * p.lp_st + h * p.lp_sh;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+
+  if constexpr (SM > 0) {
+    float ls[SM];
+#pragma unroll
+    for (int s = 0; s < SM; ++s) ls[s] = s < p.S ? lrow[s * p.lp_ss] : -INFINITY;
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SM; ++s) m = fmaxf(m, ls[s]);
+    if (m != -INFINITY) {
+      float tot = 0.0f;
+#pragma unroll
+      for (int s = 0; s < SM; ++s) tot += s < p.S ? exp2f((ls[s] - m) * kLog2e) : 0.0f;
+      lse = m + logf(tot);
+      float v[SM][8];
+#pragma unroll
+      for (int s = 0; s < SM; ++s) {
+        if (ls[s] != -INFINITY) {  // an empty partial contributes nothing and is not read
+          load8(p.parts, p.part_fp32, s * p.p_ss + t * p.p_st + h * p.p_sh + 8 * lane, v[s]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[s][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < SM; ++s) {
+        if (ls[s] == -INFINITY) continue;
+        const float w = exp2f((ls[s] - lse) * kLog2e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * v[s][i];
+      }
+    }
+  } else {
+    float m = -INFINITY;
+    for (int s = 0; s < p.S; ++s) m = fmaxf(m, lrow[s * p.lp_ss]);
+    if (m != -INFINITY) {
+      float tot = 0.0f;
+      for (int s = 0; s < p.S; ++s) tot += exp2f((lrow[s * p.lp_ss] - m) * kLog2e);
+      lse = m + logf(tot);
+      for (int s = 0; s < p.S; ++s) {
+        const float ls = lrow[s * p.lp_ss];
+        if (ls == -INFINITY) continue;  // an empty partial contributes nothing
+        const float w = exp2f((ls - lse) * kLog2e);
+        float v[8];
+        load8(p.parts, p.part_fp32, s * p.p_ss + t * p.p_st + h * p.p_sh + 8 * lane, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
+      }
+    }
+  }
+  store_out(p, t, h, lane, acc, lse);
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const int64_t pairs = (int64_t)p.T * p.H;
   const unsigned grid = (unsigned)((pairs + kMergeWaves - 1) / kMergeWaves);
-  hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(kMergeWaves * 64), 0, stream, p);
+  const dim3 g(grid), b(kMergeWaves * 64);
+  if (p.S <= 2)
+    hipLaunchKernelGGL(merge_kernel<2>, g, b, 0, stream, p);
+  else if (p.S <= 4)
+    hipLaunchKernelGGL(merge_kernel<4>, g, b, 0, stream, p);
+  else if (p.S <= 8)
+    hipLaunchKernelGGL(merge_kernel<8>, g, b, 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<0>, g, b, 0, stream, p);
   return hipGetLastError();
 }
 

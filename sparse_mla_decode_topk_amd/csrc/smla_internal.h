@@ -27,6 +27,7 @@ struct ConvertParams {
   int32_t* slots;
   int64_t slots_ld;
   int32_t* valid;
+  int32_t lg_block, lg_dcp, lg_interleave;  // log2 of block_size, dcp_size, interleave; -1: not a power of two
 };
 
 struct DecodeParams {
