@@ -7,12 +7,17 @@ shares no code, header, table or helper with it.
 """
 from .smla_oracle import (  # noqa: F401
     attention_rows,
+    bf16_encode,
     bf16_to_f64,
+    cache_write,
     convert_index,
+    dcp_local_seq_lens,
     decode_records,
+    e4m3fn_encode,
     e4m3fn_to_f64,
     flatten_bhs_lse,
     merge_lse,
+    quantize_records,
     sparse_mla_decode,
     transpose_hT_lse,
 )

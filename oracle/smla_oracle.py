@@ -35,6 +35,23 @@ Readings where the pages are silent:
 * R7 a row with no candidate (all -1, padded row, empty shard) is (out = 0,
   lse = -inf), the identity of the LSE merge; a merge whose inputs are all -inf
   is (0, -inf) too, never NaN.
+* R8 quantiser of a record (only the cache write uses it; the decode reads stored
+  bytes): per 128-value tile scale = fp32(amax / 448), or 1.0 when that is not
+  positive (amax = 0, or an underflowing quotient); each latent value becomes
+  fp32(x / scale) rounded to the nearest E4M3FN value, ties to the even code,
+  magnitudes beyond 448 saturating to 448, the sign bit kept (so -0.0 and small
+  negatives give 0x80); rope values are rounded to bf16 (nearest, ties to even).
+  The pages name the packed cache but not its quantiser; the amax / 448 tile
+  scale is the recipe of the tiny check configuration of the benchmark set.
+* R9 cache placement under DCP: a new token at request position p is written
+  only by the rank that owns p (R6) at its local position, through that rank's
+  block table; with DCP off the position goes through the request's table as is.
+  Page "FlashMLA sparse fp8 path gains DCP and MTP", "Review highlights", item 2:
+  a draft model that maps ctx_pos // block_size without DCP disagrees with the
+  target model's DCP-aware mapping.  A rank's local sequence length counts the
+  positions below the request's length that it owns (page "[Bugfix][Attention]
+  Stabilize sparse-MLA DCP for GLM PCP evals", "Root causes and fixes",
+  subsection "DCP decode rank scalar", names the helper get_dcp_local_seq_lens).
 """
 from __future__ import annotations
 
@@ -215,3 +232,87 @@ def flatten_bhs_lse(lse_bhs):
     a = np.asarray(lse_bhs)
     Bn, H, S = a.shape
     return np.transpose(a, (0, 2, 1)).reshape(Bn * S, H).copy()
+
+
+# ----------------------------------------------------------------- cache write (DCP-aware)
+
+_E4M3_POS = _E4M3_TABLE[:0x7F]  # values of codes 0x00 .. 0x7E, ascending; 0x7E = 448
+
+
+def e4m3fn_encode(x) -> np.ndarray:
+    """Nearest E4M3FN code of each value (reading R8): the nearest of the 127
+    non-negative finite values to |x| (|x| clamped to 448), the even code on a tie,
+    plus the sign bit of x.  Finite inputs only."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_hi = _E4M3_POS[hi] - a
+    d_lo = a - _E4M3_POS[lo]
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def _to_f32(x) -> np.ndarray:
+    """Round fp64 values to the nearest fp32 (numpy's cast rounds to nearest, ties even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def bf16_encode(x) -> np.ndarray:
+    """bf16 bit patterns of values already in fp32: nearest bf16, ties to even, as the
+    upper 16 bits of the fp32 pattern after adding 0x7FFF plus the lowest kept bit."""
+    b = np.ascontiguousarray(_to_f32(x)).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def quantize_records(latent, rope) -> np.ndarray:
+    """Pack tokens into fp8_ds_mla records [n, 656] (readings R1 and R8).
+
+    ``latent`` [n, 512] and ``rope`` [n, 64] hold fp32-representable values (bf16 or
+    fp32 inputs).  Per 128-value tile: scale = fp32(amax / 448) (1.0 if that is not
+    positive), code = E4M3FN-nearest of fp32(x / scale); rope is stored as bf16.
+    The fp64 quotients rounded once to fp32 equal the correctly rounded fp32 divisions.
+    """
+    lat = np.asarray(latent, dtype=np.float64).reshape(-1, LATENT)
+    n = lat.shape[0]
+    tiles = lat.reshape(n, LATENT // TILE, TILE)
+    amax = np.abs(tiles).max(axis=2)  # [n, 4]
+    scale = _to_f32(amax / 448.0).astype(np.float64)
+    scale = np.where(scale > 0.0, scale, 1.0)
+    y = _to_f32(tiles / scale[:, :, None]).astype(np.float64)
+    rec = np.zeros((n, RECORD), dtype=np.uint8)
+    rec[:, :LATENT] = e4m3fn_encode(y).reshape(n, LATENT)
+    rec[:, LATENT:LATENT + 16] = _to_f32(scale).astype("<f4").view(np.uint8).reshape(n, 16)
+    rec[:, LATENT + 16:] = bf16_encode(np.asarray(rope, dtype=np.float64).reshape(n, ROPE)).astype("<u2").view(
+        np.uint8).reshape(n, 2 * ROPE)
+    return rec
+
+
+def cache_write(latent, rope, positions, req, block_table, block_size, num_slots, dcp_size=1, dcp_rank=0,
+                interleave=1):
+    """Records of new tokens and the slots this rank writes them to (readings R8, R9).
+
+    Token i sits at request position ``positions[i]`` of request ``req[i]``; the rank
+    writes it iff it owns that position, at the slot the id-to-slot conversion gives
+    for the same position (page "FlashMLA sparse fp8 path gains DCP and MTP",
+    "Implementation breakdown" step 2 describes that conversion for reads).  A negative
+    position, a missing block or a slot outside [0, num_slots) is not written.
+    Returns (records [n, 656] uint8, slot_mapping [n] int32 with -1 = not written).
+    """
+    pos = np.asarray(positions, dtype=np.int64).reshape(-1, 1)
+    slots, _ = convert_index(pos, req, block_table, block_size, dcp_size, dcp_rank, interleave)
+    slots = slots[:, 0].astype(np.int64)
+    slots = np.where((slots >= 0) & (slots < int(num_slots)), slots, -1)
+    return quantize_records(latent, rope), slots.astype(np.int32)
+
+
+def dcp_local_seq_lens(seq_lens, dcp_size, dcp_rank, interleave=1) -> np.ndarray:
+    """Number of positions below each request's length that rank ``dcp_rank`` owns
+    (reading R9 with the ownership of R6), counted position by position."""
+    D, r, I = int(dcp_size), int(dcp_rank), int(interleave)
+    out = []
+    for L in np.asarray(seq_lens, dtype=np.int64).reshape(-1):
+        p = np.arange(max(int(L), 0), dtype=np.int64)
+        out.append(int(((p // I) % D == r).sum()))
+    return np.asarray(out, dtype=np.int32)

@@ -402,10 +402,140 @@ def test_generator_determinism():
     assert np.array_equal(c2.q_bits[:32], c1.q_bits) and np.array_equal(c2.ids[:32], c1.ids)
 
 
+# ------------------------------------------------------------------ cache write (quantiser, placement)
+
+def check_e4m3_encode(enc):
+    """The encoder against the decoder's table, the midpoints, saturation and torch's cast."""
+    vals = O.e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    assert np.array_equal(enc(vals[finite]), finite.astype(np.uint8))  # every value is its own code
+    pos = vals[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2.0  # exact in fp32: one more mantissa bit
+    got = enc(mids).astype(np.int64)
+    assert np.all(got % 2 == 0) and np.all((got == np.arange(126)) | (got == np.arange(1, 127)))
+    up = np.nextafter(mids.astype(np.float32), np.float32(np.inf)).astype(np.float64)
+    assert np.array_equal(enc(up), np.arange(1, 127, dtype=np.uint8))  # just above a midpoint: upper
+    assert np.array_equal(enc(-up), (np.arange(1, 127) | 0x80).astype(np.uint8))
+    assert list(enc(np.array([449.0, 1e30, -500.0, -0.0, 0.0, -1e-30]))) == [0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x80]
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-12, 9, 200000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc(x.astype(np.float64)), ref)
+
+
+def check_quantize(quant):
+    """Quantised records against the error bound, the tile maximum, zero tiles, torch's bf16
+    cast and the workload generator's own (torch-cast based) packer."""
+    from workload.gen import pack_records
+    rng = np.random.default_rng(11)
+    lat = rng.standard_normal((64, 512)).astype(np.float32)
+    lat[3, :128] = 0.0
+    lat[4, 128:256] = -0.0
+    lat[5, 256:384] *= np.float32(1e-30)
+    lat[6] *= np.float32(1e4)
+    rope = rng.standard_normal((64, 64)).astype(np.float32)
+    rec = quant(lat.astype(np.float64), rope.astype(np.float64))
+    assert rec.shape == (64, 656) and rec.dtype == np.uint8
+    assert np.array_equal(rec, pack_records(lat, rope))
+    sc = rec[:, 512:528].copy().view("<f4")
+    assert sc[3, 0] == 1.0 and not rec[3, :128].any()
+    assert sc[4, 1] == 1.0 and np.all(rec[4, 128:256] == 0x80)
+    codes = rec[:, :512].reshape(64, 4, 128)
+    tiles = lat.reshape(64, 4, 128)
+    nz = np.abs(tiles).max(axis=2) > 0
+    at_max = np.take_along_axis(codes, np.abs(tiles).argmax(axis=2)[..., None], axis=2)[..., 0] & 0x7F
+    assert np.all(at_max[nz] == 0x7E)  # the tile maximum encodes as +-448
+    dq = O.e4m3fn_to_f64(codes) * sc[:, :, None]
+    y = np.abs(tiles / sc[:, :, None]).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+    half_ulp = np.exp2(e - 4)  # half of 2^(e-3); subnormals share the 2^-9 step
+    assert np.all(np.abs(dq - tiles) <= half_ulp * sc[:, :, None] * (1 + 2.0 ** -20) + 1e-45)
+    rope_ref = torch.from_numpy(rope).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(rec[:, 528:].copy().view("<u2"), rope_ref)
+
+
+def check_cache_write_hand(cw):
+    """Worked by hand from the ownership rule: D = 2, block size 4, shard table of rank 1."""
+    lat = np.zeros((6, 512))
+    rope = np.zeros((6, 64))
+    pos = np.array([0, 1, 2, 3, 5, 7])
+    req = np.array([0, 0, 0, 1, 1, 1])
+    bt = np.array([[3, 0], [1, 2]])
+    # rank 1, I = 1: owns odd positions at local p // 2 -> (req 0, pos 1): bt[0][0]*4 + 0 = 12,
+    # (req 1, pos 3): local 1 -> 1*4 + 1 = 5, pos 5 -> local 2 -> 6, pos 7 -> local 3 -> 7
+    _, sm = cw(lat, rope, pos, req, bt, 4, 16, dcp_size=2, dcp_rank=1, interleave=1)
+    assert list(sm) == [-1, 12, -1, 5, 6, 7]
+    # rank 0, I = 2: owns positions 0,1 (and 4,5, 8,9, ...), local (p // 4) * 2 + p % 2
+    _, sm = cw(lat, rope, pos, req, bt, 4, 16, dcp_size=2, dcp_rank=0, interleave=2)
+    assert list(sm) == [12, 13, -1, -1, 7, -1]  # pos 5 of req 1: local 3 -> bt[1][0]*4 + 3
+    # no DCP: position p -> bt[req][p // 4] * 4 + p % 4; slot 9 and beyond are cut by num_slots
+    _, sm = cw(lat, rope, pos, req, bt, 4, 9, dcp_size=1, dcp_rank=0, interleave=1)
+    assert list(sm) == [-1, -1, -1, 7, -1, -1]  # 12, 13, 14 >= 9; pos 5, 7 of req 1 -> 9, 11 >= 9
+
+
+def check_cache_write_partition(cw):
+    """Every token is written by exactly one rank, at a slot that the id conversion of the
+    same position also yields (two oracle functions, one rule), with the same record bytes."""
+    rng = np.random.default_rng(5)
+    n, B = 40, 8
+    lat = rng.standard_normal((n, 512))
+    rope = rng.standard_normal((n, 64))
+    req = rng.integers(0, 3, n)
+    pos = rng.integers(0, 60, n)
+    for D, I in ((2, 1), (4, 1), (4, 2), (3, 3)):
+        owners = np.zeros(n, dtype=np.int64)
+        for r in range(D):
+            bt = rng.permutation(3 * 8).reshape(3, 8)
+            rec, sm = cw(lat, rope, pos, req, bt, B, 24 * B, dcp_size=D, dcp_rank=r, interleave=I)
+            owners += sm >= 0
+            assert np.array_equal(rec, O.quantize_records(lat, rope))
+            assert np.all(((pos // I) % D == r) == (sm >= 0))
+    assert np.all(owners == 1)
+
+
+def check_local_seq_lens(f):
+    """Hand examples, the closed form and the partition of every length over the ranks."""
+    assert list(f([10], 4, 0, 1)) + list(f([10], 4, 3, 1)) == [3, 2]
+    assert [int(f([10], 4, r, 2)[0]) for r in range(4)] == [4, 2, 2, 2]
+    assert list(f([0, 1, 2], 2, 1, 1)) == [0, 0, 1]
+    rng = np.random.default_rng(3)
+    L = rng.integers(0, 5000, 50)
+    for D, I in ((2, 1), (4, 1), (8, 1), (4, 3)):
+        tot = np.zeros(50, dtype=np.int64)
+        for r in range(D):
+            got = f(L, D, r, I).astype(np.int64)
+            closed = (L // (I * D)) * I + np.clip(L % (I * D) - r * I, 0, I)
+            assert np.array_equal(got, closed)
+            tot += got
+        assert np.array_equal(tot, L)
+
+
+def test_e4m3_encode():
+    check_e4m3_encode(O.e4m3fn_encode)
+
+
+def test_quantize_records():
+    check_quantize(O.quantize_records)
+
+
+def test_cache_write_hand():
+    check_cache_write_hand(O.cache_write)
+
+
+def test_cache_write_partition():
+    check_cache_write_partition(O.cache_write)
+
+
+def test_dcp_local_seq_lens():
+    check_local_seq_lens(O.dcp_local_seq_lens)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 ORIG = {name: getattr(O, name) for name in
-        ("decode_records", "e4m3fn_to_f64", "attention_rows", "convert_index", "merge_lse")}
+        ("decode_records", "e4m3fn_to_f64", "attention_rows", "convert_index", "merge_lse", "e4m3fn_encode",
+         "quantize_records", "cache_write", "dcp_local_seq_lens")}
 
 
 def _mutants():
@@ -444,7 +574,32 @@ def _mutants():
         out, lse = ORIG["attention_rows"](q, slots, cache, n, sc)
         return out[..., ::-1].copy(), lse
 
+    def encode_ties_away(x):
+        x = np.asarray(x, dtype=np.float64)
+        return ORIG["e4m3fn_encode"](x * (1 + 2.0 ** -30))  # midpoints go up, not to even
+
+    def quantize_wrong_max(lat, rope):
+        return ORIG["quantize_records"](np.asarray(lat) * (447.0 / 448.0), rope)
+
+    def quantize_rope_truncated(lat, rope):
+        rec = ORIG["quantize_records"](lat, rope).copy()
+        r32 = np.asarray(rope, dtype=np.float32).reshape(rec.shape[0], 64)
+        rec[:, 528:] = (r32.view(np.uint32) >> 16).astype("<u2").view(np.uint8).reshape(rec.shape[0], 128)
+        return rec
+
+    def cache_write_dcp_blind(lat, rope, pos, req, bt, B, n, dcp_size=1, dcp_rank=0, interleave=1):
+        rec, sm = ORIG["cache_write"](lat, rope, pos, req, bt, B, n)
+        own = (np.asarray(pos) // interleave) % dcp_size == dcp_rank
+        return rec, np.where(own, sm, -1).astype(np.int32)
+
+    def local_lens_ceil(L, D, r, I=1):
+        return ORIG["dcp_local_seq_lens"](np.asarray(L) + 1, D, r, I)
+
     return {
+        "e4m3fn_encode": [encode_ties_away],
+        "quantize_records": [quantize_wrong_max, quantize_rope_truncated],
+        "cache_write": [cache_write_dcp_blind],
+        "dcp_local_seq_lens": [local_lens_ceil],
         "decode_records": [drop_rope, wrong_scale_index],
         "e4m3fn_to_f64": [sign_flip_e4m3],
         "attention_rows": [lse_without_max, qk_transposed_value],
@@ -468,6 +623,11 @@ def _all_pins():
                                    attention=O.attention_rows),
         lambda: check_merge_identities(O.merge_lse),
         lambda: check_page_example(O.attention_rows, O.merge_lse),
+        lambda: check_e4m3_encode(O.e4m3fn_encode),
+        lambda: check_quantize(O.quantize_records),
+        lambda: check_cache_write_hand(O.cache_write),
+        lambda: check_cache_write_partition(O.cache_write),
+        lambda: check_local_seq_lens(O.dcp_local_seq_lens),
     ]
 
 
