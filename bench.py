@@ -9,7 +9,8 @@ LSE merge into bf16 out and (T, H) LSE.
 Prints one JSON line on stdout.  `value` is query rows per second of the whole step with
 every input resident in HBM.  `roofline` covers the decode kernel: algorithmic bytes and
 flops per launch over its mean launch time (HIP events on the launch stream).
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same rows.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same rows.  `cache_write`
+times the fp8_ds_mla cache write of one 32768-token chunk beside the step.
 """
 from __future__ import annotations
 
@@ -52,6 +53,39 @@ def roofline_entry(byts, flops, seconds):
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
 
 
+def time_cache_write(dev, iters=20, n=32768):
+    """fp8_ds_mla cache write of one n-token prefill chunk (bf16 latent and rope, no DCP):
+    mean launch time over `iters` launches (HIP events on the launch stream) and its rate
+    against HBM, counting 1152 B read + 8 B of position and request + 656 B written + 4 B
+    of slot mapping per token."""
+    import numpy as np
+    import torch
+    import sparse_mla_decode_topk_amd as smla
+    g = torch.Generator(device="cpu").manual_seed(5)
+    lat = torch.randn((n, 512), generator=g).to(torch.bfloat16).to(dev)
+    rope = torch.randn((n, 64), generator=g).to(torch.bfloat16).to(dev)
+    pos = torch.arange(n, dtype=torch.int32, device=dev)
+    req = torch.zeros(n, dtype=torch.int32, device=dev)
+    bt = torch.randperm(n // 64, generator=g).to(torch.int32).reshape(1, -1).to(dev)
+    cache = torch.empty((n, 656), dtype=torch.uint8, device=dev)
+    sm = torch.empty((n,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        smla.cache_write(lat, rope, pos, req, bt, cache, 64, slot_mapping=sm)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        smla.cache_write(lat, rope, pos, req, bt, cache, 64, slot_mapping=sm)
+        b.record(stream)
+    torch.cuda.synchronize()
+    s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    byts = n * (1152 + 8 + 656 + 4)
+    gbps = byts / s / 1e9
+    return {"tokens": n, "dtype": "bf16", "us": round(s * 1e6, 2), "algorithmic_bytes": byts,
+            "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w, budget_s):
     """fp64 oracle of the same DCP2 step (converts, shard attention, merge) over the rows in
     order, wrapping around, until the time budget is spent; rows/s over the rows done."""
@@ -87,8 +121,8 @@ def cpu_baseline(w, budget_s):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "102c27ab85ec5cac774037c7f5253ca54708e2167fd5ce8d88b5b4fb240b94a2",
-                  "fetch_bytes": 227313802, "write_bytes": 67246144}
+DECODE_TRAFFIC = {"sources_sha256": "1a3b1e073c8596634ef5f7babcbac1f75646cd528307f804a5134c7c91d9fb7c",
+                  "fetch_bytes": 227323725, "write_bytes": 67245264}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
 
@@ -214,6 +248,7 @@ def main():
         ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], out_bytes=2)
         unsharded = {"decode_us": round(un_s * 1e6, 2), "tflops": round(uf / un_s / 1e12, 1),
                      "kv_gbps": round(656 * nvalid[0] / un_s / 1e9, 1), "roofline": roofline_entry(ub, uf, un_s)}
+    cache_write = time_cache_write(dev)
     if args.copy_mib > 0:
         n = args.copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -236,6 +271,7 @@ def main():
     }
     if unsharded is not None:
         line["unsharded_decode"] = unsharded
+    line["cache_write"] = cache_write
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

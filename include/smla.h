@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 1
+#define SMLA_ABI_VERSION 2
 
 enum smla_status {
   SMLA_OK = 0,
@@ -174,6 +174,51 @@ int sparse_mla_merge_lse(const void* out_parts, int32_t part_dtype, int64_t p_st
                          int64_t lp_stride_h, int32_t S, int32_t T, int32_t H, void* out, int32_t out_dtype,
                          int64_t o_stride_t, int64_t o_stride_h, float* lse, int64_t l_stride_t,
                          int64_t l_stride_h, hipStream_t stream);
+
+/*
+ * sparse_mla_cache_write - quantise new tokens into fp8_ds_mla records and store each
+ * at the slot this DCP rank owns for it.
+ *
+ * Placement follows the id-to-slot rule of sparse_mla_convert_index applied to the
+ * token's request position ([P-FlashMLA] "Implementation breakdown" step 2; "Review
+ * highlights" item 2: a slot mapping of ctx_pos / block_size that ignores DCP
+ * disagrees with the DCP-aware mapping the reads use).  For token i < N with
+ * p = positions[i] and b = req_id[i]: if p < 0, or dcp_size > 1 and this rank does not
+ * own p ((p / I) % D != dcp_rank), or the block is missing (b outside [0, bt_rows),
+ * block >= bt_width, table entry < 0), or the slot is >= num_slots, nothing is
+ * written and slot_mapping[i] = -1; otherwise the record goes to that slot and
+ * slot_mapping[i] is the slot.
+ *
+ * Record contents (the pages do not give the quantiser): per 128-value latent tile
+ * scale = fp32(amax / 448), 1.0 if that is not positive; code = the e4m3fn value
+ * nearest to fp32(x / scale), ties to the even code, magnitudes above 448
+ * saturating to 448, the sign bit of x kept; rope = nearest-even bf16 of the input.
+ * Inputs must be finite.
+ *
+ * latent    [N, 512] at latent + i*latent_stride (dims contiguous), in_dtype SMLA_BF16 or
+ *           SMLA_FP32; 16-byte aligned rows.  rope [N, 64] at rope + i*rope_stride, same
+ *           dtype, element-aligned.
+ * positions, req_id  int32 [N]; block_table int32 [bt_rows, bt_ld] (this rank's table).
+ * kv_cache  [num_slots, 656] bytes, 16-byte aligned; slot_mapping int32 [N] or NULL.
+ * Two tokens that map to the same slot race (the caller keeps positions distinct).
+ * Requirements as for sparse_mla_convert_index; dcp_size * interleave <= 2^30.
+ */
+int sparse_mla_cache_write(const void* latent, int64_t latent_stride, const void* rope, int64_t rope_stride,
+                           int32_t in_dtype, const int32_t* positions, const int32_t* req_id,
+                           const int32_t* block_table, int64_t bt_ld, int32_t bt_rows, int32_t bt_width, int32_t N,
+                           int32_t block_size, int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
+                           uint8_t* kv_cache, int64_t num_slots, int32_t* slot_mapping, hipStream_t stream);
+
+/*
+ * sparse_mla_dcp_local_seq_lens - how many positions below each request's length the
+ * rank owns: local_seq_lens[i] = #{ p in [0, seq_lens[i]) : (p / I) % D == dcp_rank }
+ * = (L / (I*D)) * I + clamp(L % (I*D) - dcp_rank*I, 0, I), 0 for L <= 0.
+ * [P-Stab] "Root causes and fixes", "DCP decode rank scalar" (get_dcp_local_seq_lens;
+ * the rank travels as a kernel argument, so no per-call device scalar is built).
+ * seq_lens, local_seq_lens: int32 [R], 4-byte aligned.
+ */
+int sparse_mla_dcp_local_seq_lens(const int32_t* seq_lens, int32_t R, int32_t dcp_size, int32_t dcp_rank,
+                                  int32_t interleave, int32_t* local_seq_lens, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,8 @@ What it follows (the three pages this project is built from):
   (vllm-project/vllm pull request 55879), "Root causes and fixes", subsection
   "Zero-local-sequence DCP warmup rank" (a shard with no local rows emits -inf LSE).
 
-Readings where the pages are silent:
+Readings where the pages are silent (R8-R12, on layouts, causality and tolerances,
+need no code of their own here):
 
 * R1 record layout: 656 bytes = 512 e4m3fn codes, 4 fp32 LE scales (scale i for
   latent dims 128i..128i+127), 64 bf16 LE rope values.  The pages give only the
@@ -35,7 +36,7 @@ Readings where the pages are silent:
 * R7 a row with no candidate (all -1, padded row, empty shard) is (out = 0,
   lse = -inf), the identity of the LSE merge; a merge whose inputs are all -inf
   is (0, -inf) too, never NaN.
-* R8 quantiser of a record (only the cache write uses it; the decode reads stored
+* R13 quantiser of a record (only the cache write uses it; the decode reads stored
   bytes): per 128-value tile scale = fp32(amax / 448), or 1.0 when that is not
   positive (amax = 0, or an underflowing quotient); each latent value becomes
   fp32(x / scale) rounded to the nearest E4M3FN value, ties to the even code,
@@ -43,7 +44,7 @@ Readings where the pages are silent:
   negatives give 0x80); rope values are rounded to bf16 (nearest, ties to even).
   The pages name the packed cache but not its quantiser; the amax / 448 tile
   scale is the recipe of the tiny check configuration of the benchmark set.
-* R9 cache placement under DCP: a new token at request position p is written
+* R14 cache placement under DCP: a new token at request position p is written
   only by the rank that owns p (R6) at its local position, through that rank's
   block table; with DCP off the position goes through the request's table as is.
   Page "FlashMLA sparse fp8 path gains DCP and MTP", "Review highlights", item 2:
@@ -240,7 +241,7 @@ _E4M3_POS = _E4M3_TABLE[:0x7F]  # values of codes 0x00 .. 0x7E, ascending; 0x7E 
 
 
 def e4m3fn_encode(x) -> np.ndarray:
-    """Nearest E4M3FN code of each value (reading R8): the nearest of the 127
+    """Nearest E4M3FN code of each value (reading R13): the nearest of the 127
     non-negative finite values to |x| (|x| clamped to 448), the even code on a tie,
     plus the sign bit of x.  Finite inputs only."""
     x = np.asarray(x, dtype=np.float64)
@@ -267,7 +268,7 @@ def bf16_encode(x) -> np.ndarray:
 
 
 def quantize_records(latent, rope) -> np.ndarray:
-    """Pack tokens into fp8_ds_mla records [n, 656] (readings R1 and R8).
+    """Pack tokens into fp8_ds_mla records [n, 656] (readings R1 and R13).
 
     ``latent`` [n, 512] and ``rope`` [n, 64] hold fp32-representable values (bf16 or
     fp32 inputs).  Per 128-value tile: scale = fp32(amax / 448) (1.0 if that is not
@@ -291,7 +292,7 @@ def quantize_records(latent, rope) -> np.ndarray:
 
 def cache_write(latent, rope, positions, req, block_table, block_size, num_slots, dcp_size=1, dcp_rank=0,
                 interleave=1):
-    """Records of new tokens and the slots this rank writes them to (readings R8, R9).
+    """Records of new tokens and the slots this rank writes them to (readings R13, R14).
 
     Token i sits at request position ``positions[i]`` of request ``req[i]``; the rank
     writes it iff it owns that position, at the slot the id-to-slot conversion gives
@@ -309,7 +310,7 @@ def cache_write(latent, rope, positions, req, block_table, block_size, num_slots
 
 def dcp_local_seq_lens(seq_lens, dcp_size, dcp_rank, interleave=1) -> np.ndarray:
     """Number of positions below each request's length that rank ``dcp_rank`` owns
-    (reading R9 with the ownership of R6), counted position by position."""
+    (reading R14 with the ownership of R6), counted position by position."""
     D, r, I = int(dcp_size), int(dcp_rank), int(interleave)
     out = []
     for L in np.asarray(seq_lens, dtype=np.int64).reshape(-1):

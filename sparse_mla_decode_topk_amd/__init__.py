@@ -10,13 +10,17 @@ from ._binding import (  # noqa: F401
     RECORD_BYTES,
     SmlaError,
     abi_version,
+    cache_write,
     convert_index,
+    dcp_local_seq_lens,
     decode,
     decode_workspace_size,
     lib_path,
     load_library,
     merge_lse,
+    sparse_mla_cache_write,
     sparse_mla_convert_index,
+    sparse_mla_dcp_local_seq_lens,
     sparse_mla_decode,
     sparse_mla_decode_workspace_size,
     sparse_mla_merge_lse,

@@ -65,6 +65,11 @@ def load_library():
         lib.sparse_mla_merge_lse.restype = ctypes.c_int
         lib.sparse_mla_merge_lse.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I32,
                                              _I64, _I64, _P, _I64, _I64, _P]
+        lib.sparse_mla_cache_write.restype = ctypes.c_int
+        lib.sparse_mla_cache_write.argtypes = [_P, _I64, _P, _I64, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32,
+                                               _I32, _I32, _P, _I64, _P, _P]
+        lib.sparse_mla_dcp_local_seq_lens.restype = ctypes.c_int
+        lib.sparse_mla_dcp_local_seq_lens.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P]
         _lib = lib
         return lib
 
@@ -93,6 +98,18 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int) -> None:
         raise ValueError(f"{name} must be on a GPU device")
 
 
+def _st(t: torch.Tensor, d: int) -> int:
+    """Stride of dim d in elements.  A dim of size 1 may carry any stride in torch (0 included);
+    the C calls validate strides, so such a dim reports the stride a contiguous tensor would
+    have there (its value is never used to address memory)."""
+    if t.shape[d] > 1:
+        return t.stride(d)
+    n = 1
+    for k in range(d + 1, t.dim()):
+        n *= t.shape[k]
+    return n
+
+
 def _dtype_code(dtype: torch.dtype) -> int:
     if dtype == torch.bfloat16:
         return _BF16
@@ -117,6 +134,14 @@ def sparse_mla_decode(*args) -> int:
 
 def sparse_mla_merge_lse(*args) -> int:
     return load_library().sparse_mla_merge_lse(*args)
+
+
+def sparse_mla_cache_write(*args) -> int:
+    return load_library().sparse_mla_cache_write(*args)
+
+
+def sparse_mla_dcp_local_seq_lens(*args) -> int:
+    return load_library().sparse_mla_dcp_local_seq_lens(*args)
 
 
 decode_workspace_size = sparse_mla_decode_workspace_size
@@ -163,8 +188,8 @@ def convert_index(topk_ids: torch.Tensor, req_id_per_token: torch.Tensor, block_
     valid = torch.empty((T,), dtype=torch.int32, device=topk_ids.device) if with_valid_count else None
     R, W = block_table.shape
     st = sparse_mla_convert_index(
-        topk_ids.data_ptr(), topk_ids.stride(0), req_id_per_token.data_ptr(), block_table.data_ptr(),
-        block_table.stride(0), R, W, T, K, block_size, dcp_size, dcp_rank, interleave, out.data_ptr(), out.stride(0),
+        topk_ids.data_ptr(), _st(topk_ids, 0), req_id_per_token.data_ptr(), block_table.data_ptr(),
+        _st(block_table, 0), R, W, T, K, block_size, dcp_size, dcp_rank, interleave, out.data_ptr(), _st(out, 0),
         valid.data_ptr() if valid is not None else None, _stream(topk_ids.device))
     _check("sparse_mla_convert_index", st)
     return out, valid
@@ -214,9 +239,9 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax
         pad = (-ws_ptr) % 256
         ws_ptr, ws_bytes = ws_ptr + pad, ws_bytes - pad
     st = sparse_mla_decode(
-        q.data_ptr(), q.stride(0), q.stride(1), kv_cache.data_ptr(), kv_cache.shape[0], slots.data_ptr(),
-        slots.stride(0), T, H, K, float(softmax_scale), out.data_ptr(), _dtype_code(out.dtype), out.stride(0),
-        out.stride(1), lse.data_ptr(), lse.stride(0), lse.stride(1), num_splits, ws_ptr, ws_bytes, _stream(dev))
+        q.data_ptr(), _st(q, 0), _st(q, 1), kv_cache.data_ptr(), kv_cache.shape[0], slots.data_ptr(),
+        _st(slots, 0), T, H, K, float(softmax_scale), out.data_ptr(), _dtype_code(out.dtype), _st(out, 0),
+        _st(out, 1), lse.data_ptr(), _st(lse, 0), _st(lse, 1), num_splits, ws_ptr, ws_bytes, _stream(dev))
     _check("sparse_mla_decode", st)
     return out, lse
 
@@ -241,9 +266,66 @@ def merge_lse(out_parts: torch.Tensor, lse_parts: torch.Tensor, out: Optional[to
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     _need(lse, "lse", torch.float32, 2)
     st = sparse_mla_merge_lse(
-        out_parts.data_ptr(), _dtype_code(out_parts.dtype), out_parts.stride(0), out_parts.stride(1),
-        out_parts.stride(2), lse_parts.data_ptr(), lse_parts.stride(0), lse_parts.stride(1), lse_parts.stride(2),
-        S, T, H, out.data_ptr(), _dtype_code(out.dtype), out.stride(0), out.stride(1), lse.data_ptr(), lse.stride(0),
-        lse.stride(1), _stream(dev))
+        out_parts.data_ptr(), _dtype_code(out_parts.dtype), _st(out_parts, 0), _st(out_parts, 1),
+        _st(out_parts, 2), lse_parts.data_ptr(), _st(lse_parts, 0), _st(lse_parts, 1), _st(lse_parts, 2),
+        S, T, H, out.data_ptr(), _dtype_code(out.dtype), _st(out, 0), _st(out, 1), lse.data_ptr(), _st(lse, 0),
+        _st(lse, 1), _stream(dev))
     _check("sparse_mla_merge_lse", st)
     return out, lse
+
+
+def cache_write(latent: torch.Tensor, rope: torch.Tensor, positions: torch.Tensor, req_id: torch.Tensor,
+                block_table: torch.Tensor, kv_cache: torch.Tensor, block_size: int, dcp_size: int = 1,
+                dcp_rank: int = 0, interleave: int = 1, slot_mapping: Optional[torch.Tensor] = None,
+                with_slot_mapping: bool = True) -> Optional[torch.Tensor]:
+    """Quantise tokens latent [N,512] / rope [N,64] (bf16 or fp32) into kv_cache [num_slots,656]
+    at the slots this DCP rank owns; returns slot_mapping [N] (-1 = not written here)."""
+    _need(latent, "latent", latent.dtype, 2)
+    _need(rope, "rope", latent.dtype, 2)
+    _need(positions, "positions", torch.int32, 1)
+    _need(req_id, "req_id", torch.int32, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(kv_cache, "kv_cache", torch.uint8, 2)
+    N = latent.shape[0]
+    if latent.shape[1] != LATENT_DIM or latent.stride(1) != 1 or tuple(rope.shape) != (N, ROPE_DIM) or \
+            rope.stride(1) != 1:
+        raise ValueError("latent must be [N,512] and rope [N,64], both with contiguous dims")
+    if positions.shape[0] != N or req_id.shape[0] != N or (N > 1 and (positions.stride(0) != 1 or
+                                                                      req_id.stride(0) != 1)):
+        raise ValueError("positions and req_id must be contiguous [N]")
+    if kv_cache.shape[1] != RECORD_BYTES or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_slots,656] uint8 tensor")
+    if block_table.shape[1] > 1 and block_table.stride(1) != 1:
+        raise ValueError("block_table needs a contiguous last dimension")
+    if slot_mapping is None and with_slot_mapping:
+        slot_mapping = torch.empty((N,), dtype=torch.int32, device=latent.device)
+    if slot_mapping is not None:
+        _need(slot_mapping, "slot_mapping", torch.int32, 1)
+        if slot_mapping.shape[0] != N or (N > 1 and slot_mapping.stride(0) != 1):
+            raise ValueError("slot_mapping must be contiguous [N]")
+    R, W = block_table.shape
+    st = sparse_mla_cache_write(
+        latent.data_ptr(), _st(latent, 0), rope.data_ptr(), _st(rope, 0), _dtype_code(latent.dtype),
+        positions.data_ptr(), req_id.data_ptr(), block_table.data_ptr(), _st(block_table, 0), R, W, N, block_size,
+        dcp_size, dcp_rank, interleave, kv_cache.data_ptr(), kv_cache.shape[0],
+        slot_mapping.data_ptr() if slot_mapping is not None else None, _stream(latent.device))
+    _check("sparse_mla_cache_write", st)
+    return slot_mapping
+
+
+def dcp_local_seq_lens(seq_lens: torch.Tensor, dcp_size: int, dcp_rank: int, interleave: int = 1,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Positions below each request's length that DCP rank ``dcp_rank`` owns, [R] int32."""
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    R = seq_lens.shape[0]
+    if R > 1 and seq_lens.stride(0) != 1:
+        raise ValueError("seq_lens must be contiguous")
+    if out is None:
+        out = torch.empty((R,), dtype=torch.int32, device=seq_lens.device)
+    _need(out, "out", torch.int32, 1)
+    if out.shape[0] != R or (R > 1 and out.stride(0) != 1):
+        raise ValueError("out must be contiguous [R]")
+    st = sparse_mla_dcp_local_seq_lens(seq_lens.data_ptr(), R, dcp_size, dcp_rank, interleave, out.data_ptr(),
+                                       _stream(seq_lens.device))
+    _check("sparse_mla_dcp_local_seq_lens", st)
+    return out

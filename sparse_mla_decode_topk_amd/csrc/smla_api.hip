@@ -225,4 +225,60 @@ int sparse_mla_merge_lse(const void* out_parts, int32_t part_dtype, int64_t p_st
   return launch_merge(p, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
+int sparse_mla_cache_write(const void* latent, int64_t latent_stride, const void* rope, int64_t rope_stride,
+                           int32_t in_dtype, const int32_t* positions, const int32_t* req_id,
+                           const int32_t* block_table, int64_t bt_ld, int32_t bt_rows, int32_t bt_width, int32_t N,
+                           int32_t block_size, int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
+                           uint8_t* kv_cache, int64_t num_slots, int32_t* slot_mapping, hipStream_t stream) {
+  if (N < 0 || num_slots < 0 || latent_stride < 0 || rope_stride < 0) return SMLA_ERR_INVALID_ARG;
+  if (in_dtype != SMLA_BF16 && in_dtype != SMLA_FP32) return SMLA_ERR_INVALID_ARG;
+  if (block_size < 1 || dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1)
+    return SMLA_ERR_INVALID_ARG;
+  if (bt_rows < 1 || bt_width < 1 || bt_ld < bt_width) return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)dcp_size * interleave > (1 << 30)) return SMLA_ERR_UNSUPPORTED;
+  if (N == 0) return SMLA_OK;
+  if (!latent || !rope || !positions || !req_id || !block_table || (num_slots > 0 && !kv_cache))
+    return SMLA_ERR_INVALID_ARG;
+  if (N > 1 && (latent_stride < kLatent || rope_stride < kRope)) return SMLA_ERR_INVALID_ARG;
+  const int64_t lvec = in_dtype == SMLA_FP32 ? 4 : 8;  // elements per 16 bytes
+  const int64_t esz = in_dtype == SMLA_FP32 ? 4 : 2;
+  if (!aligned(latent, 16) || latent_stride % lvec != 0 || !aligned(rope, esz) || !aligned(positions, 4) ||
+      !aligned(req_id, 4) || !aligned(block_table, 4) || (kv_cache && !aligned(kv_cache, 16)) ||
+      (slot_mapping && !aligned(slot_mapping, 4)))
+    return SMLA_ERR_MISALIGNED;
+  CacheWriteParams p{};
+  p.latent = latent;
+  p.rope = rope;
+  p.latent_st = latent_stride;
+  p.rope_st = rope_stride;
+  p.in_fp32 = in_dtype == SMLA_FP32;
+  p.pos = positions;
+  p.req = req_id;
+  p.bt = block_table;
+  p.bt_ld = bt_ld;
+  p.bt_rows = bt_rows;
+  p.bt_width = bt_width;
+  p.N = N;
+  p.block_size = block_size;
+  p.dcp_size = dcp_size;
+  p.dcp_rank = dcp_rank;
+  p.interleave = interleave;
+  p.cache = kv_cache;
+  p.num_slots = num_slots;
+  p.slot_mapping = slot_mapping;
+  return launch_cache_write(p, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+int sparse_mla_dcp_local_seq_lens(const int32_t* seq_lens, int32_t R, int32_t dcp_size, int32_t dcp_rank,
+                                  int32_t interleave, int32_t* local_seq_lens, hipStream_t stream) {
+  if (R < 0 || dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1) return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)dcp_size * interleave > (1 << 30)) return SMLA_ERR_UNSUPPORTED;
+  if (R == 0) return SMLA_OK;
+  if (!seq_lens || !local_seq_lens) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(seq_lens, 4) || !aligned(local_seq_lens, 4)) return SMLA_ERR_MISALIGNED;
+  return launch_local_lens(seq_lens, R, dcp_size, dcp_rank, interleave, local_seq_lens, stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -64,6 +64,23 @@ struct MergeParams {
   int64_t l_st, l_sh;
 };
 
+struct CacheWriteParams {
+  const void* latent;  // [N, 512] bf16 or fp32, row stride latent_st elements
+  const void* rope;    // [N, 64] same dtype, row stride rope_st elements
+  int64_t latent_st, rope_st;
+  int32_t in_fp32;
+  const int32_t* pos;  // [N] position of the token in its request
+  const int32_t* req;  // [N] request of the token
+  const int32_t* bt;
+  int64_t bt_ld;
+  int32_t bt_rows, bt_width;
+  int32_t N, block_size, dcp_size, dcp_rank, interleave;
+  uint8_t* cache;
+  int64_t num_slots;
+  int32_t* slot_mapping;  // [N] optional
+  int32_t lg_block, lg_dcp, lg_interleave;  // log2 of block_size, dcp_size, interleave; -1: not a power of two
+};
+
 struct DecodePlan {
   int32_t head_blocks;  // workgroups per row along heads
   int32_t splits;       // top-k ranges per row
@@ -74,5 +91,8 @@ struct DecodePlan {
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
+hipError_t launch_local_lens(const int32_t* seq_lens, int32_t R, int32_t D, int32_t r, int32_t I, int32_t* out,
+                             hipStream_t stream);
 
 }  // namespace smla

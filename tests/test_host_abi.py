@@ -30,7 +30,8 @@ def lib():
 def test_header_lists_the_calls():
     names = declared_functions()
     for n in ("smla_abi_version", "smla_status_string", "sparse_mla_convert_index", "sparse_mla_decode",
-              "sparse_mla_decode_workspace_size", "sparse_mla_merge_lse"):
+              "sparse_mla_decode_workspace_size", "sparse_mla_merge_lse", "sparse_mla_cache_write",
+              "sparse_mla_dcp_local_seq_lens"):
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smla_abi_version() == 1
+    assert lib.smla_abi_version() == 2
     for st in range(0, 7):
         assert isinstance(lib.smla_status_string(st), bytes) and lib.smla_status_string(st)
 
@@ -134,6 +135,40 @@ def merge_call(lib, **kw):
 ])
 def test_merge_validation(lib, kw, want):
     assert merge_call(lib, **kw) == want
+
+
+def cache_write_call(lib, **kw):
+    a = dict(lat=A16, lst=512, rope=A16, rst=64, dt=0, pos=A16, req=A16, bt=A16, bt_ld=4, bt_rows=2, bt_width=4, N=3,
+             B=64, D=1, r=0, I=1, kv=A16, ns=100, sm=A16)
+    a.update(kw)
+    return lib.sparse_mla_cache_write(a["lat"], a["lst"], a["rope"], a["rst"], a["dt"], a["pos"], a["req"], a["bt"],
+                                      a["bt_ld"], a["bt_rows"], a["bt_width"], a["N"], a["B"], a["D"], a["r"], a["I"],
+                                      a["kv"], a["ns"], a["sm"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=-1), INVALID), (dict(ns=-1), INVALID), (dict(dt=2), INVALID), (dict(B=0), INVALID), (dict(D=0), INVALID),
+    (dict(D=2, r=2), INVALID), (dict(I=0), INVALID), (dict(bt_ld=2), INVALID), (dict(bt_rows=0), INVALID),
+    (dict(lst=256), INVALID), (dict(rst=32), INVALID), (dict(lat=None), INVALID), (dict(rope=None), INVALID),
+    (dict(pos=None), INVALID), (dict(req=None), INVALID), (dict(bt=None), INVALID), (dict(kv=None), INVALID),
+    (dict(D=1 << 16, I=1 << 15), UNSUPPORTED),
+    (dict(lat=A16 + 8), MISALIGNED), (dict(lst=516), MISALIGNED), (dict(dt=1, lst=514), MISALIGNED),
+    (dict(rope=A16 + 1), MISALIGNED), (dict(dt=1, rope=A16 + 2), MISALIGNED), (dict(pos=A16 + 2), MISALIGNED),
+    (dict(kv=A16 + 8), MISALIGNED), (dict(sm=A16 + 1), MISALIGNED),
+    (dict(N=0), OK), (dict(N=0, lat=None, kv=None), OK),
+])
+def test_cache_write_validation(lib, kw, want):
+    assert cache_write_call(lib, **kw) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((A16, -1, 1, 0, 1, A16), INVALID), ((A16, 4, 0, 0, 1, A16), INVALID), ((A16, 4, 2, 2, 1, A16), INVALID),
+    ((A16, 4, 2, 0, 0, A16), INVALID), ((None, 4, 2, 0, 1, A16), INVALID), ((A16, 4, 2, 0, 1, None), INVALID),
+    ((A16 + 2, 4, 2, 0, 1, A16), MISALIGNED), ((A16, 4, 2, 0, 1, A16 + 1), MISALIGNED),
+    ((None, 0, 2, 1, 1, None), OK),
+])
+def test_local_seq_lens_validation(lib, args, want):
+    assert lib.sparse_mla_dcp_local_seq_lens(*args, None) == want
 
 
 def test_binding_refuses_cpu_tensors():
