@@ -12,6 +12,7 @@ from .smla_oracle import (  # noqa: F401
     cache_write,
     convert_index,
     dcp_local_seq_lens,
+    dense_decode,
     decode_records,
     e4m3fn_encode,
     e4m3fn_to_f64,

@@ -317,3 +317,31 @@ def dcp_local_seq_lens(seq_lens, dcp_size, dcp_rank, interleave=1) -> np.ndarray
         p = np.arange(max(int(L), 0), dtype=np.int64)
         out.append(int(((p // I) % D == r).sum()))
     return np.asarray(out, dtype=np.int32)
+
+
+# ----------------------------------------------------------------- dense decode (whole context)
+
+def dense_decode(q, cache, num_slots, block_table, seq_lens, S, block_size, sm_scale, dcp_size=1, dcp_rank=0,
+                 interleave=1):
+    """Whole-context MLA decode with S query tokens per request, on one DCP rank.
+
+    Page "FlashMLA sparse fp8 path gains DCP and MTP", "Implementation breakdown" step 5
+    and the flashmla.py ``forward_mqa`` snippet: the dense path attends over the request's
+    whole paged context and returns an LSE of layout [batch, heads, seq_len] that the DCP
+    merge consumes flattened to [batch * seq_len, heads] (row b*S + s).  Query token s of
+    request b sits at position seq_lens[b] - S + s and sees every position up to its own
+    (reading R9, the same causality as the top-k rows); under DCP a rank sees the positions
+    it owns (R6).  Written as the top-k attention with the list of all those positions.
+    q [B*S, H, 576]; returns out [B*S, H, 512], lse [B*S, H] in fp64.
+    """
+    L = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    nb = L.shape[0]
+    K = max(1, int(L.max()) if nb else 1)
+    ids = np.full((nb * S, K), -1, dtype=np.int64)
+    for b in range(nb):
+        for s in range(S):
+            n = max(0, int(L[b]) - S + s + 1)
+            ids[b * S + s, :n] = np.arange(n)
+    req = np.repeat(np.arange(nb), S)
+    slots, _ = convert_index(ids, req, block_table, block_size, dcp_size, dcp_rank, interleave)
+    return attention_rows(q, slots, cache, num_slots, sm_scale)

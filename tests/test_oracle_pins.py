@@ -531,11 +531,75 @@ def test_dcp_local_seq_lens():
     check_local_seq_lens(O.dcp_local_seq_lens)
 
 
+# ------------------------------------------------------------------ dense decode (whole context, MTP rows)
+
+def check_dense_sdpa(dense):
+    """Dense decode against torch's scaled_dot_product_attention over each request's logical
+    context (records decoded by torch casts), a causal mask per query position, fp64; the LSE
+    comes out in the pages' native [batch, heads, seq_len] layout and is flattened with the
+    oracle's own (pinned) flatten to the [batch * seq_len, heads] rows."""
+    from workload import make_dense
+    S = 3
+    w = make_dense(21, n_req=3, S=S, H=8, ctx=[70, 9, 2], B=16)
+    out, lse = dense(w.q_f32(), w.cache, w.cache.num_slots, w.block_table, w.ctx, S, w.block_size, w.sm_scale)
+    q = torch.from_numpy(w.q_f32().astype(np.float64))
+    nb = len(w.ctx)
+    native_lse = np.full((nb, w.H, S), -np.inf)
+    native_out = np.zeros((nb, S, w.H, 512))
+    for b in range(nb):
+        L = int(w.ctx[b])
+        lat, rope = torch_decode_records(w.cache.gather(_slots_in_order(w.block_table[b], L, w.block_size)))
+        k = torch.from_numpy(np.concatenate([lat, rope], axis=1))[None, None]  # [1,1,L,576]
+        v = torch.from_numpy(lat)[None, None]
+        qb = q[b * S:(b + 1) * S].permute(1, 0, 2)[None]  # [1,H,S,576]
+        pos = L - S + np.arange(S)
+        visible = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])  # [S, L]
+        if not visible.any():
+            continue
+        o = torch.nn.functional.scaled_dot_product_attention(qb, k.expand(1, w.H, L, 576), v.expand(1, w.H, L, 512),
+                                                             attn_mask=visible, scale=w.sm_scale)
+        sc = (qb @ k.transpose(-1, -2))[0] * w.sm_scale  # [H,S,L]
+        l = torch.logsumexp(sc.masked_fill(~visible[None], -np.inf), dim=-1)  # [H,S]
+        for s in range(S):
+            if visible[s].any():
+                native_out[b, s] = o[0, :, s].numpy()
+                native_lse[b, :, s] = l[:, s].numpy()
+    ref_lse = O.flatten_bhs_lse(native_lse)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0) < 1e-10
+    assert np.max(np.abs(out - native_out.reshape(nb * S, w.H, 512)), initial=0) < 1e-10
+    assert np.all(out[~fin] == 0)
+
+
+def check_dense_dcp_merge(dense, merge):
+    """The merge of the D shards' dense partials equals the unsharded dense decode."""
+    from workload import make_dense
+    for D in (2, 4):
+        w = make_dense(30 + D, n_req=2, S=2, H=4, ctx=[45, 3], B=8, D=D)
+        args = (w.ctx, 2, w.block_size, w.sm_scale)
+        ref_o, ref_l = dense(w.q_f32(), w.cache, w.cache.num_slots, w.block_table, *args)
+        parts = [dense(w.q_f32(), sh.cache, sh.cache.num_slots, sh.block_table, *args, dcp_size=D, dcp_rank=sh.rank)
+                 for sh in w.shards]
+        o, l = merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        assert np.max(np.abs(o - ref_o)) < 1e-12 and np.array_equal(np.isneginf(l), np.isneginf(ref_l))
+        fin = np.isfinite(ref_l)
+        assert np.max(np.abs(l[fin] - ref_l[fin]), initial=0) < 1e-12
+
+
+def test_dense_sdpa():
+    check_dense_sdpa(O.dense_decode)
+
+
+def test_dense_dcp_merge():
+    check_dense_dcp_merge(O.dense_decode, O.merge_lse)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 ORIG = {name: getattr(O, name) for name in
         ("decode_records", "e4m3fn_to_f64", "attention_rows", "convert_index", "merge_lse", "e4m3fn_encode",
-         "quantize_records", "cache_write", "dcp_local_seq_lens")}
+         "quantize_records", "cache_write", "dcp_local_seq_lens", "dense_decode")}
 
 
 def _mutants():
@@ -595,7 +659,17 @@ def _mutants():
     def local_lens_ceil(L, D, r, I=1):
         return ORIG["dcp_local_seq_lens"](np.asarray(L) + 1, D, r, I)
 
+    def dense_causal_short(q, cache, n, bt, L, S, B, sc, dcp_size=1, dcp_rank=0, interleave=1):
+        return ORIG["dense_decode"](q, cache, n, bt, np.asarray(L) - 1, S, B, sc, dcp_size, dcp_rank, interleave)
+
+    def dense_rows_s_major(q, cache, n, bt, L, S, B, sc, dcp_size=1, dcp_rank=0, interleave=1):
+        o, l = ORIG["dense_decode"](q, cache, n, bt, L, S, B, sc, dcp_size, dcp_rank, interleave)
+        nb = len(np.asarray(L))
+        perm = np.arange(nb * S).reshape(nb, S).T.reshape(-1)
+        return o[perm], l[perm]
+
     return {
+        "dense_decode": [dense_causal_short, dense_rows_s_major],
         "e4m3fn_encode": [encode_ties_away],
         "quantize_records": [quantize_wrong_max, quantize_rope_truncated],
         "cache_write": [cache_write_dcp_blind],
@@ -628,6 +702,8 @@ def _all_pins():
         lambda: check_cache_write_hand(O.cache_write),
         lambda: check_cache_write_partition(O.cache_write),
         lambda: check_local_seq_lens(O.dcp_local_seq_lens),
+        lambda: check_dense_sdpa(O.dense_decode),
+        lambda: check_dense_dcp_merge(O.dense_decode, O.merge_lse),
     ]
 
 

@@ -17,6 +17,7 @@ from .gen import (  # noqa: F401
     SparseCache,
     Workload,
     make_config,
+    make_dense,
     make_random,
     pack_records,
 )

@@ -438,3 +438,31 @@ def make_random(seed: int, *, T: int, H: int, K: int, ctx: int, B: int = 64, D: 
             real.append(np.unique(sel[sel >= 0]))
     return _finish(f"rand{seed}", rng, H=H, K=K, B=B, D=D, out_dtype=out_dtype, ids=ids, req=req,
                    row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts)
+
+
+def make_dense(seed: int, *, n_req: int, S: int, H: int, ctx, B: int = 64, D: int = 1,
+               out_dtype: str = "bf16") -> Workload:
+    """Whole-context (dense) decode workload with S query tokens per request (MTP shape).
+
+    Request b has context length ctx[b] (an int applies to all); its S query tokens are its
+    last S positions, row b*S + s at position ctx[b] - S + s.  ``ids`` lists, per row, every
+    position up to and including the row's own (causal), padded with -1 to K = max ctx, so the
+    same workload also feeds the top-k path.  Every in-context position holds a real record.
+    Draw order: block tables, shard tables, q, records.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctxs = np.broadcast_to(np.asarray(ctx, dtype=np.int64), (n_req,)).copy()
+    bt_pack = _block_table(rng, -(-ctxs // B))
+    shard_bts = _shard_tables(rng, ctxs, B, D)
+    T = n_req * S
+    K = max(1, int(ctxs.max()) if n_req else 1)
+    req = np.repeat(np.arange(n_req), S)
+    row_pos = np.array([int(ctxs[b]) - S + s for b in range(n_req) for s in range(S)], dtype=np.int64)
+    ids = np.full((T, K), -1, dtype=np.int32)
+    for t in range(T):
+        n = max(0, int(row_pos[t]) + 1)
+        ids[t, :n] = np.arange(n, dtype=np.int32)
+    real = [np.arange(c) for c in ctxs]
+    return _finish(f"dense{seed}", rng, H=H, K=K, B=B, D=D, out_dtype=out_dtype, ids=ids, req=req,
+                   row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts,
+                   note=f"dense, S={S}")
