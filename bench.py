@@ -86,6 +86,96 @@ def time_cache_write(dev, iters=20, n=32768):
             "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def dense_algorithmic(w):
+    """Bytes and flops of one whole-context decode of workload ``w``: every record of every
+    request once (the S rows and the head blocks of a request share them), q, out (bf16),
+    LSE and the slot lists; 2176 flops per (visible position, head)."""
+    import numpy as np
+    visible = int(np.maximum(w.row_pos + 1, 0).sum())
+    K = int(w.ctx.max())
+    byts = 656 * int(w.ctx.sum()) + w.T * w.H * 576 * 2 + w.T * w.H * (512 * 2 + 4) + w.T * K * 4 * 2
+    return byts, FLOP_PER_VALID_ID_PER_HEAD * w.H * visible
+
+
+def main_dense(args):
+    """--workload dense: the whole-context decode of 32 requests x 4 MTP tokens (T = 128 rows),
+    H = 128, context 4096 per request, one call per step."""
+    import numpy as np
+    import torch
+    import sparse_mla_decode_topk_amd as smla
+    from workload import make_dense
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    smla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    S, n_req, ctx, H = 4, 32, 4096, 128
+    log(f"generating dense workload ({n_req} requests x {S} MTP tokens, H={H}, context {ctx}) ...")
+    w = make_dense(2000, n_req=n_req, S=S, H=H, ctx=ctx, B=64)
+    q = w.q_torch().to(dev)
+    caches = [w.cache.to_device(dev) for _ in range(max(1, args.replicas))]
+    bt = torch.from_numpy(w.block_table).to(dev)
+    seq = torch.from_numpy(w.ctx.astype(np.int32)).to(dev)
+    out = torch.empty((w.T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(i):
+        smla.dense_decode(q, caches[i % len(caches)], bt, seq, S, w.sm_scale, w.block_size, ctx, out=out, lse=lse)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        run(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    byts, flops = dense_algorithmic(w)
+    roof = roofline_entry(byts, flops, call_s)
+    roof.update({"traffic": None, "kernel": "dense_slots_kernel + decode_kernel (one whole-context decode call)",
+                 "launch_us": round(call_s * 1e6, 2), "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops)})
+    line = {
+        "metric": METRIC, "value": round(w.T * args.steps / wall, 1), "unit": "query-rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"dense_mtp: {n_req} req x {S} MTP tokens (T={w.T}), H={H}, whole context {ctx} "
+                               f"(causal per MTP token), fp8_ds_mla cache, no DCP", "T": w.T, "H": H, "S": S,
+                   "ctx": ctx, "block_size": w.block_size, "cache_replicas": len(caches)},
+        "kv_gbps": round(656 * int(np.maximum(w.row_pos + 1, 0).sum()) / call_s / 1e9, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.smla_oracle as O
+        log("timing the CPU oracle on a bounded sample ...")
+        rows_done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_budget:
+            t = rows_done % w.T
+            sub = w.rows([t])
+            sl, _ = O.convert_index(sub.ids, sub.req, sub.block_table, sub.block_size)
+            O.attention_rows(sub.q_f32(), sl, sub.cache, sub.cache.num_slots, sub.sm_scale)
+            rows_done += 1
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(rows_done / el, 3), "unit": "query-rows/s", "cores": blas_threads(),
+                                "kind": "oracle",
+                                "sample": f"{rows_done} rows of the same workload in order through the fp64 numpy "
+                                          f"oracle (each row: its causal position list, block-table conversion, "
+                                          f"attention); {el:.1f} s on {blas_threads()} host CPUs"}
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(w, budget_s):
     """fp64 oracle of the same DCP2 step (converts, shard attention, merge) over the rows in
     order, wrapping around, until the time budget is spent; rows/s over the rows done."""
@@ -152,6 +242,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unsharded", action="store_true",
                     help="also time the unsharded decode of the same rows (reported beside the step)")
+    ap.add_argument("--workload", choices=("c3", "dense"), default="c3",
+                    help="c3: the DCP2 MTP step (default); dense: the whole-context MTP decode")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -159,6 +251,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
               f"the DCP shards are simulated on one device", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "dense":
+        main_dense(args)
+        return
 
     import numpy as np
     import torch

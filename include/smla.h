@@ -141,7 +141,7 @@ size_t sparse_mla_decode_workspace_size(int32_t T, int32_t H, int32_t K, int32_t
  *          what it needs with a kernel of its own); may be NULL when the size is 0.
  *          Calls that share a workspace must be ordered (same stream); concurrent
  *          ones race.
- * Supported: 1 <= H <= 128, H % 16 == 0; K <= 2048 * num_splits (automatic splits
+ * Supported: 1 <= H <= 128, H % 16 == 0; K <= 4096 * num_splits (automatic splits
  * always satisfy this); softmax_scale finite and > 0.
  */
 int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
@@ -174,6 +174,48 @@ int sparse_mla_merge_lse(const void* out_parts, int32_t part_dtype, int64_t p_st
                          int64_t lp_stride_h, int32_t S, int32_t T, int32_t H, void* out, int32_t out_dtype,
                          int64_t o_stride_t, int64_t o_stride_h, float* lse, int64_t l_stride_t,
                          int64_t l_stride_h, hipStream_t stream);
+
+/*
+ * sparse_mla_dense_decode_workspace_size - bytes of workspace sparse_mla_dense_decode
+ * needs: the per-row slot lists (B*S rows of the width below, 4 bytes each) plus the
+ * workspace of the decode that reads them (automatic split plan on the current device).
+ * 0 for invalid sizes.
+ */
+size_t sparse_mla_dense_decode_workspace_size(int32_t B, int32_t S, int32_t H, int32_t max_seq_len,
+                                              int32_t dcp_size, int32_t interleave);
+
+/*
+ * sparse_mla_dense_decode - MLA decode over each request's whole paged context, with S
+ * query tokens per request (speculative / MTP decode), on one DCP rank.
+ *
+ * [P-FlashMLA] "Implementation breakdown" step 5 and the flashmla.py forward_mqa snippet:
+ * the dense decode returns out and an LSE that the DCP merge consumes as
+ * [batch * seq_len, heads]; here the rows are written in that order directly (row
+ * t = b*S + s), so no flatten copy exists.
+ *
+ * Row t = b*S + s is query token s of request b, at position p = seq_lens[b] - S + s; it
+ * attends to every position 0..p of request b (p < 0: no position, out = 0, lse = -inf).
+ * With dcp_size = D > 1 the rank sees only the positions it owns ((pos / I) % D ==
+ * dcp_rank), stored at its local positions 0, 1, ... through block_table (this rank's
+ * table, [bt_rows, bt_ld]); the partial results of the D ranks merge with
+ * sparse_mla_merge_lse into the unsharded result.  Everything else (q, kv_cache, out, lse,
+ * softmax_scale, H, their layouts and alignment) is as in sparse_mla_decode with T = B*S.
+ *
+ * seq_lens  int32 [B]; every entry must be <= max_seq_len, which sizes the slot lists
+ *           (a longer context is cut at max_seq_len).  Requests b >= bt_rows have no
+ *           context on this rank.
+ * workspace at least sparse_mla_dense_decode_workspace_size(B, S, H, max_seq_len,
+ *           dcp_size, interleave) bytes, 256-byte aligned; never NULL when B*S > 0.
+ * Supported: the slot-list width (max_seq_len, or the rank-0 share of it under DCP) up to
+ * 262144 (64 splits of 4096 entries); H as in sparse_mla_decode.
+ */
+int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                            int64_t num_slots, const int32_t* block_table, int64_t bt_ld, int32_t bt_rows,
+                            int32_t bt_width, const int32_t* seq_lens, int32_t B, int32_t S, int32_t H,
+                            int32_t block_size, int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
+                            int32_t max_seq_len, float softmax_scale, void* out, int32_t out_dtype,
+                            int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                            int64_t lse_stride_h, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * sparse_mla_cache_write - quantise new tokens into fp8_ds_mla records and store each

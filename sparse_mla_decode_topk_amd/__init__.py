@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     dcp_local_seq_lens,
     decode,
     decode_workspace_size,
+    dense_decode,
     lib_path,
     load_library,
     merge_lse,
@@ -23,6 +24,8 @@ from ._binding import (  # noqa: F401
     sparse_mla_dcp_local_seq_lens,
     sparse_mla_decode,
     sparse_mla_decode_workspace_size,
+    sparse_mla_dense_decode,
+    sparse_mla_dense_decode_workspace_size,
     sparse_mla_merge_lse,
     workspace_for,
 )

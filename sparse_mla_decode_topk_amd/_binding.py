@@ -65,6 +65,12 @@ def load_library():
         lib.sparse_mla_merge_lse.restype = ctypes.c_int
         lib.sparse_mla_merge_lse.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I32,
                                              _I64, _I64, _P, _I64, _I64, _P]
+        lib.sparse_mla_dense_decode_workspace_size.restype = _SZ
+        lib.sparse_mla_dense_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32]
+        lib.sparse_mla_dense_decode.restype = ctypes.c_int
+        lib.sparse_mla_dense_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _I64, _I32, _I32, _P, _I32, _I32, _I32,
+                                                _I32, _I32, _I32, _I32, _I32, _F32, _P, _I32, _I64, _I64, _P, _I64,
+                                                _I64, _P, _SZ, _P]
         lib.sparse_mla_cache_write.restype = ctypes.c_int
         lib.sparse_mla_cache_write.argtypes = [_P, _I64, _P, _I64, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32,
                                                _I32, _I32, _P, _I64, _P, _P]
@@ -134,6 +140,15 @@ def sparse_mla_decode(*args) -> int:
 
 def sparse_mla_merge_lse(*args) -> int:
     return load_library().sparse_mla_merge_lse(*args)
+
+
+def sparse_mla_dense_decode_workspace_size(B: int, S: int, H: int, max_seq_len: int, dcp_size: int = 1,
+                                           interleave: int = 1) -> int:
+    return int(load_library().sparse_mla_dense_decode_workspace_size(B, S, H, max_seq_len, dcp_size, interleave))
+
+
+def sparse_mla_dense_decode(*args) -> int:
+    return load_library().sparse_mla_dense_decode(*args)
 
 
 def sparse_mla_cache_write(*args) -> int:
@@ -329,3 +344,54 @@ def dcp_local_seq_lens(seq_lens: torch.Tensor, dcp_size: int, dcp_rank: int, int
                                        _stream(seq_lens.device))
     _check("sparse_mla_dcp_local_seq_lens", st)
     return out
+
+
+_dense_ws = {}
+
+
+def dense_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                 S: int, softmax_scale: float, block_size: int, max_seq_len: int, dcp_size: int = 1,
+                 dcp_rank: int = 0, interleave: int = 1, out: Optional[torch.Tensor] = None,
+                 out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Whole-context decode: q [B*S,H,576] bf16 (row b*S + s), seq_lens [B] int32 (each <= max_seq_len).
+    Returns out [B*S,H,512] and lse [B*S,H] (the [batch * seq_len, heads] rows)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_cache, "kv_cache", torch.uint8, 2)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    T, H, D = q.shape
+    nb = seq_lens.shape[0]
+    if D != HEAD_DIM or q.stride(2) != 1:
+        raise ValueError("q must be [B*S,H,576] with contiguous dims")
+    if T != nb * S:
+        raise ValueError(f"q has {T} rows, seq_lens and S give {nb} x {S}")
+    if kv_cache.shape[1] != RECORD_BYTES or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_slots,656] uint8 tensor")
+    if (block_table.shape[1] > 1 and block_table.stride(1) != 1) or (nb > 1 and seq_lens.stride(0) != 1):
+        raise ValueError("block_table and seq_lens need a contiguous last dimension")
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=out_dtype, device=dev)
+    if tuple(out.shape) != (T, H, LATENT_DIM) or out.stride(2) != 1:
+        raise ValueError("out must be [B*S,H,512] with contiguous dims")
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(lse, "lse", torch.float32, 2)
+    if workspace is None:
+        need = sparse_mla_dense_decode_workspace_size(nb, S, H, max_seq_len, dcp_size, interleave)
+        key = (dev.index if dev.index is not None else torch.cuda.current_device())
+        workspace = _dense_ws.get(key)
+        if workspace is None or workspace.numel() < need + 256:
+            workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+            _dense_ws[key] = workspace
+    ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    pad = (-ws_ptr) % 256
+    R, W = block_table.shape
+    st = sparse_mla_dense_decode(
+        q.data_ptr(), _st(q, 0), _st(q, 1), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(),
+        _st(block_table, 0), R, W, seq_lens.data_ptr(), nb, S, H, block_size, dcp_size, dcp_rank, interleave,
+        max_seq_len, float(softmax_scale), out.data_ptr(), _dtype_code(out.dtype), _st(out, 0), _st(out, 1),
+        lse.data_ptr(), _st(lse, 0), _st(lse, 1), ws_ptr + pad, ws_bytes - pad, _stream(dev))
+    _check("sparse_mla_dense_decode", st)
+    return out, lse

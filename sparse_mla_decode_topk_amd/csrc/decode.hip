@@ -82,6 +82,8 @@ constexpr int kRopeChunk = kRopeOffset / 16;    // 33
 
 static_assert(kRecordBytes % 16 == 0, "records are whole 16-byte chunks");
 static_assert(kAhead >= 1 && kAhead <= 3, "load waits below cover up to 3 tiles ahead");
+static_assert(kHB * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile buffers");
+static_assert(kHB * (kLatent / 4) % kThreads == 0 && kThreads % (kLatent / 4) == 0, "combine item split");
 
 struct Shared {
   uint8_t stage[kStages * kTileBytes];
@@ -468,37 +470,71 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
   }
 }
 
-// The last split of a (row, head block) to arrive merges every split's partial.
-__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, int tid) {
-  for (int item = tid; item < bk.nh * (kLatent / 4); item += kThreads) {
-    const int hrel = item / (kLatent / 4);
-    const int d4 = item - hrel * (kLatent / 4);
-    const int h = bk.h_lo + hrel;
+// The last split of a (row, head block) to arrive merges every split's partial.  First one
+// thread per head turns the splits' (max, sum) into normalised weights in LDS (and writes the
+// head's LSE); then each thread owns 4 dims of every fourth head and, split by split, loads
+// all of its partial rows before accumulating them, so the merge costs one memory round trip
+// per split rather than several per output element.
+__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, Shared& sh, int tid) {
+  float* wts = reinterpret_cast<float*>(sh.stage);  // [head][split]; the tile buffers are free now
+  if (tid < bk.nh) {
+    const int h = bk.h_lo + tid;
     const float* ml = p.ws_ml + ((int64_t)bk.row * p.splits * p.H + h) * 2;  // split sp at + sp * H * 2
     float M = -INFINITY;
+#pragma unroll 8
     for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2));
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.0f;
     if (M != -INFINITY) {
+#pragma unroll 8
       for (int sp = 0; sp < p.splits; ++sp) {
         const float ms = __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2);
-        if (ms == -INFINITY) continue;
-        const float w = fast_exp2(ms - M);
+        const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
+        wts[tid * p.splits + sp] = w;
         L += w * __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2 + 1);
-        const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + h;
-        acc += w * __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
       }
     }
     const bool empty = !(L > 0.0f);
-    acc *= empty ? 0.0f : 1.0f / L;
+    const float inv = empty ? 0.0f : 1.0f / L;
+    for (int sp = 0; sp < p.splits; ++sp) wts[tid * p.splits + sp] = empty ? 0.0f : wts[tid * p.splits + sp] * inv;
+    p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
+  }
+  __syncthreads();
+  constexpr int kPerThread = kHB * (kLatent / 4) / kThreads;  // 16 (head, 4-dim) items per thread
+  const int d4 = tid % (kLatent / 4);
+  const int h0 = tid / (kLatent / 4);  // heads h0, h0 + 4, ... (wave-uniform)
+  f32x4 acc[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < p.splits; ++sp) {
+    f32x4 part[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int hl = h0 + (kThreads / (kLatent / 4)) * i;
+      part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (hl < bk.nh && wts[hl * p.splits + sp] != 0.0f) {
+        const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + bk.h_lo + hl;
+        part[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int hl = h0 + (kThreads / (kLatent / 4)) * i;
+      if (hl < bk.nh) acc[i] += wts[hl * p.splits + sp] * part[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int hl = h0 + (kThreads / (kLatent / 4)) * i;
+    if (hl >= bk.nh) continue;
+    const int h = bk.h_lo + hl;
     if (p.out_fp32) {
       float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc;
+      *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc[i];
     } else {
       __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<bf16x4*>(orow + 4 * d4) = bf16x4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+      *reinterpret_cast<bf16x4*>(orow + 4 * d4) =
+          bf16x4{(__bf16)acc[i][0], (__bf16)acc[i][1], (__bf16)acc[i][2], (__bf16)acc[i][3]};
     }
-    if (d4 == 0) p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
   }
 }
 
@@ -568,8 +604,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     value_role(p, sh, bk, wave - 4, lane);
   if (p.splits == 1) return;
 
-  // ---- split-K: the last split of this (row, head block) to arrive combines all of them
-  __threadfence();
+  // ---- split-K: the last split of this (row, head block) to arrive combines all of them.
+  // The barrier completes every wave's partial stores; one device-scope acquire-release
+  // atomic by one thread then publishes them and, in the last split, makes the other splits'
+  // partials visible to the workgroup after the second barrier.  (A device-scope fence in
+  // every thread would make each wave write back the L2 of its XCD: measured twice as slow.)
   __syncthreads();
   if (tid == 0) {
     const int old = __hip_atomic_fetch_add(p.ws_cnt + (int64_t)bk.row * p.head_blocks + bk.hb, 1, __ATOMIC_ACQ_REL,
@@ -578,8 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   }
   __syncthreads();
   if (!sh.last_flag) return;
-  __threadfence();
-  combine_splits(p, bk, tid);
+  combine_splits(p, bk, sh, tid);
 }
 
 __global__ void zero_counters(int32_t* cnt, int64_t n) {

@@ -122,11 +122,17 @@ size_t sparse_mla_decode_workspace_size(int32_t T, int32_t H, int32_t K, int32_t
   return make_plan(T, H, K, num_splits, num_splits > 0 ? 256 : device_cus()).ws_total;
 }
 
-int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
-                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
-                      int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
-                      int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
-                      int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch parameters of a decode call; nothing is launched.  Shared by the
+// top-k decode and the whole-context decode (which builds its slot lists first).
+int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache, int64_t num_slots,
+                   const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H, int32_t K, float softmax_scale,
+                   void* out, int32_t out_dtype, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                   int64_t lse_stride_t, int64_t lse_stride_h, int32_t num_splits, void* workspace,
+                   size_t workspace_bytes, DecodeParams& p, DecodePlan& plan) {
   if (T < 0 || H < 1 || K < 0 || num_slots < 0) return SMLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return SMLA_ERR_INVALID_ARG;
   if (out_dtype != SMLA_BF16 && out_dtype != SMLA_FP32) return SMLA_ERR_INVALID_ARG;
@@ -144,14 +150,14 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
       out_stride_h % ovec != 0 || !aligned(lse, 4))
     return SMLA_ERR_MISALIGNED;
   const int cus = num_splits > 0 ? 256 : device_cus();
-  const DecodePlan plan = make_plan(T, H, K, num_splits, cus);
+  plan = make_plan(T, H, K, num_splits, cus);
   if ((int64_t)K > (int64_t)plan.splits * kMaxEntriesPerSplit) return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)T * plan.head_blocks * plan.splits > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
   if (plan.ws_total > 0) {
     if (!workspace || workspace_bytes < plan.ws_total) return SMLA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SMLA_ERR_MISALIGNED;
   }
-  DecodeParams p{};
+  p = DecodeParams{};
   p.q = static_cast<const uint16_t*>(q);
   p.q_st = q_stride_t;
   p.q_sh = q_stride_h;
@@ -180,6 +186,84 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
     p.ws_ml = reinterpret_cast<float*>(ws + plan.ws_cnt_bytes);
     p.ws_o = reinterpret_cast<float*>(ws + plan.ws_cnt_bytes + plan.ws_ml_bytes);
   }
+  return SMLA_OK;
+}
+
+// Bytes of the slot lists a whole-context decode keeps at the front of its workspace.
+size_t dense_slots_bytes(int64_t T, int64_t K) { return round_up((size_t)T * (size_t)K * sizeof(int32_t), 256); }
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
+                      int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
+                      int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DecodeParams p;
+  DecodePlan plan;
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, T, H, K,
+                                softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse, lse_stride_t,
+                                lse_stride_h, num_splits, workspace, workspace_bytes, p, plan);
+  if (st != SMLA_OK || T == 0) return st;
+  return launch_decode(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+size_t sparse_mla_dense_decode_workspace_size(int32_t B, int32_t S, int32_t H, int32_t max_seq_len,
+                                              int32_t dcp_size, int32_t interleave) {
+  if (B <= 0 || S < 1 || H < 1 || max_seq_len < 0 || dcp_size < 1 || interleave < 1) return 0;
+  if ((int64_t)dcp_size * interleave > (1 << 30) || (int64_t)B * S > 0x7fffffffLL) return 0;
+  const int64_t T = (int64_t)B * S;
+  const int64_t K = dense_list_width(max_seq_len, dcp_size, interleave);
+  if (K > (int64_t)kMaxSplits * kMaxEntriesPerSplit) return 0;
+  return dense_slots_bytes(T, K) + make_plan((int32_t)T, H, (int32_t)K, 0, device_cus()).ws_total;
+}
+
+int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                            int64_t num_slots, const int32_t* block_table, int64_t bt_ld, int32_t bt_rows,
+                            int32_t bt_width, const int32_t* seq_lens, int32_t B, int32_t S, int32_t H,
+                            int32_t block_size, int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
+                            int32_t max_seq_len, float softmax_scale, void* out, int32_t out_dtype,
+                            int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                            int64_t lse_stride_h, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || S < 1 || H < 1 || max_seq_len < 0 || block_size < 1) return SMLA_ERR_INVALID_ARG;
+  if (dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1) return SMLA_ERR_INVALID_ARG;
+  if (bt_rows < 1 || bt_width < 1 || bt_ld < bt_width) return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)dcp_size * interleave > (1 << 30) || (int64_t)B * S > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
+  const int64_t T = (int64_t)B * S;
+  const int64_t K = dense_list_width(max_seq_len, dcp_size, interleave);
+  if (K > (int64_t)kMaxSplits * kMaxEntriesPerSplit) return SMLA_ERR_UNSUPPORTED;
+  if (T == 0) return SMLA_OK;
+  if (!seq_lens || !block_table) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(seq_lens, 4) || !aligned(block_table, 4)) return SMLA_ERR_MISALIGNED;
+  if (!workspace) return SMLA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SMLA_ERR_MISALIGNED;
+  const size_t lists = dense_slots_bytes(T, K);
+  if (workspace_bytes < lists) return SMLA_ERR_WORKSPACE;
+  int32_t* slots = static_cast<int32_t*>(workspace);
+  DecodeParams p;
+  DecodePlan plan;
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, K, (int32_t)T, H,
+                                (int32_t)K, softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse,
+                                lse_stride_t, lse_stride_h, 0, static_cast<char*>(workspace) + lists,
+                                workspace_bytes - lists, p, plan);
+  if (st != SMLA_OK) return st;
+  DenseSlotParams d{};
+  d.seq_lens = seq_lens;
+  d.bt = block_table;
+  d.bt_ld = bt_ld;
+  d.bt_rows = bt_rows;
+  d.bt_width = bt_width;
+  d.T = (int32_t)T;
+  d.S = S;
+  d.K = (int32_t)K;
+  d.block_size = block_size;
+  d.dcp_size = dcp_size;
+  d.dcp_rank = dcp_rank;
+  d.interleave = interleave;
+  d.slots = slots;
+  if (launch_dense_slots(d, stream) != hipSuccess) return SMLA_ERR_HIP;
   return launch_decode(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 

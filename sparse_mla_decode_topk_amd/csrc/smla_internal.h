@@ -12,7 +12,7 @@ constexpr int kHeadDim = kLatent + kRope;  // 576
 constexpr int kRecordBytes = 656;          // 512 e4m3 codes + 4 fp32 scales + 64 bf16 rope
 constexpr int kScaleOffset = 512;
 constexpr int kRopeOffset = 528;
-constexpr int kMaxEntriesPerSplit = 2048;  // slot entries one decode workgroup compacts
+constexpr int kMaxEntriesPerSplit = 4096;  // slot entries one decode workgroup compacts
 constexpr int kMaxSplits = 64;
 constexpr int kHeadsPerBlock = 64;           // heads one decode workgroup covers
 
@@ -81,6 +81,15 @@ struct CacheWriteParams {
   int32_t lg_block, lg_dcp, lg_interleave;  // log2 of block_size, dcp_size, interleave; -1: not a power of two
 };
 
+struct DenseSlotParams {
+  const int32_t* seq_lens;  // [B] context length of each request
+  const int32_t* bt;
+  int64_t bt_ld;
+  int32_t bt_rows, bt_width;
+  int32_t T, S, K, block_size, dcp_size, dcp_rank, interleave;
+  int32_t* slots;  // [T, K] out
+};
+
 struct DecodePlan {
   int32_t head_blocks;  // workgroups per row along heads
   int32_t splits;       // top-k ranges per row
@@ -92,6 +101,8 @@ hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
+hipError_t launch_dense_slots(const DenseSlotParams& p, hipStream_t stream);
+int64_t dense_list_width(int64_t max_seq_len, int dcp_size, int interleave);
 hipError_t launch_local_lens(const int32_t* seq_lens, int32_t R, int32_t D, int32_t r, int32_t I, int32_t* out,
                              hipStream_t stream);
 

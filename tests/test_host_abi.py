@@ -31,7 +31,7 @@ def test_header_lists_the_calls():
     names = declared_functions()
     for n in ("smla_abi_version", "smla_status_string", "sparse_mla_convert_index", "sparse_mla_decode",
               "sparse_mla_decode_workspace_size", "sparse_mla_merge_lse", "sparse_mla_cache_write",
-              "sparse_mla_dcp_local_seq_lens"):
+              "sparse_mla_dcp_local_seq_lens", "sparse_mla_dense_decode", "sparse_mla_dense_decode_workspace_size"):
         assert n in names
 
 
@@ -98,7 +98,7 @@ def decode_call(lib, **kw):
     (dict(kv=None), INVALID), (dict(q=A16 + 2), MISALIGNED), (dict(qsh=580), MISALIGNED),
     (dict(kv=A16 + 8), MISALIGNED), (dict(slots=A16 + 2), MISALIGNED), (dict(out=A16 + 8), MISALIGNED),
     (dict(odt=1, osh=514), MISALIGNED), (dict(lse=A16 + 2), MISALIGNED),
-    (dict(K=4096, sld=4096, splits=1), UNSUPPORTED), (dict(K=128, sld=128, splits=2), WORKSPACE),
+    (dict(K=8192, sld=8192, splits=1), UNSUPPORTED), (dict(K=128, sld=128, splits=2), WORKSPACE),
     (dict(K=128, sld=128, splits=2, ws=A16 + 64, wsb=1 << 30), MISALIGNED),
     (dict(T=0), OK), (dict(T=0, q=None, out=None), OK),
 ])
@@ -169,6 +169,40 @@ def test_cache_write_validation(lib, kw, want):
 ])
 def test_local_seq_lens_validation(lib, args, want):
     assert lib.sparse_mla_dcp_local_seq_lens(*args, None) == want
+
+
+def dense_call(lib, **kw):
+    a = dict(q=A16, qst=128 * 576, qsh=576, kv=A16, ns=100, bt=A16, bt_ld=8, bt_rows=2, bt_width=8, sl=A16, B=2, S=4,
+             H=128, blk=64, D=1, r=0, I=1, maxlen=512, scale=0.07, out=A16, odt=0, ost=128 * 512, osh=512, lse=A16,
+             lst=128, lsh=1, ws=A16 * 16, wsb=1 << 30)
+    a.update(kw)
+    return lib.sparse_mla_dense_decode(a["q"], a["qst"], a["qsh"], a["kv"], a["ns"], a["bt"], a["bt_ld"], a["bt_rows"],
+                                       a["bt_width"], a["sl"], a["B"], a["S"], a["H"], a["blk"], a["D"], a["r"], a["I"],
+                                       a["maxlen"], a["scale"], a["out"], a["odt"], a["ost"], a["osh"], a["lse"],
+                                       a["lst"], a["lsh"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), INVALID), (dict(S=0), INVALID), (dict(H=0), INVALID), (dict(maxlen=-1), INVALID),
+    (dict(blk=0), INVALID), (dict(D=2, r=2), INVALID), (dict(I=0), INVALID), (dict(bt_ld=4), INVALID),
+    (dict(bt_rows=0), INVALID), (dict(sl=None), INVALID), (dict(bt=None), INVALID), (dict(q=None), INVALID),
+    (dict(scale=0.0), INVALID), (dict(H=40), UNSUPPORTED), (dict(maxlen=(1 << 18) + 1), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=A16 * 16 + 16), MISALIGNED),
+    (dict(sl=A16 + 2), MISALIGNED), (dict(q=A16 + 2), MISALIGNED),
+    (dict(B=0), OK), (dict(B=0, q=None, ws=None), OK),
+])
+def test_dense_validation(lib, kw, want):
+    assert dense_call(lib, **kw) == want
+
+
+def test_dense_workspace_size(lib):
+    # slot lists (B*S rows of the list width) ahead of the decode's own workspace
+    r = lambda x: (x + 255) // 256 * 256
+    ws = lib.sparse_mla_dense_decode_workspace_size(2, 4, 128, 512, 1, 1)
+    assert ws >= r(8 * 512 * 4)
+    assert lib.sparse_mla_dense_decode_workspace_size(2, 4, 128, 1000, 2, 1) >= r(8 * 500 * 4)
+    assert lib.sparse_mla_dense_decode_workspace_size(0, 4, 128, 512, 1, 1) == 0
+    assert lib.sparse_mla_dense_decode_workspace_size(2, 4, 128, (1 << 18) + 1, 1, 1) == 0
 
 
 def test_binding_refuses_cpu_tensors():
