@@ -211,8 +211,8 @@ def cpu_baseline(w, budget_s):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "1a3b1e073c8596634ef5f7babcbac1f75646cd528307f804a5134c7c91d9fb7c",
-                  "fetch_bytes": 227323725, "write_bytes": 67245264}
+DECODE_TRAFFIC = {"sources_sha256": "d239eb26099fa8559844d93e673055858e91d13d729c4ef56e11bd1ea6d97ece",
+                  "fetch_bytes": 227312368, "write_bytes": 67247644}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
 
