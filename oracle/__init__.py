@@ -14,11 +14,13 @@ from .smla_oracle import (  # noqa: F401
     dcp_local_seq_lens,
     dense_decode,
     decode_records,
+    decode_records_bf16,
     e4m3fn_encode,
     e4m3fn_to_f64,
     flatten_bhs_lse,
     merge_lse,
     quantize_records,
     sparse_mla_decode,
+    sparse_mla_decode_bf16,
     transpose_hT_lse,
 )

@@ -36,6 +36,9 @@ need no code of their own here):
 * R7 a row with no candidate (all -1, padded row, empty shard) is (out = 0,
   lse = -inf), the identity of the LSE merge; a merge whose inputs are all -inf
   is (0, -inf) too, never NaN.
+* R15 plain bf16 record (the layout the pages contrast with fp8_ds_mla: 576
+  values, 1152 bytes per token): 512 latent then 64 rope values, little-endian
+  bf16; key = all 576, value = the 512 latent values.
 * R13 quantiser of a record (only the cache write uses it; the decode reads stored
   bytes): per 128-value tile scale = fp32(amax / 448), or 1.0 when that is not
   positive (amax = 0, or an underflowing quotient); each latent value becomes
@@ -106,6 +109,21 @@ def decode_records(rec) -> tuple:
     return latent.reshape(n, LATENT), bf16_to_f64(rope_bits).reshape(n, ROPE)
 
 
+BF16_RECORD = 2 * (LATENT + ROPE)  # 1152
+
+
+def decode_records_bf16(rec) -> tuple:
+    """Plain bf16 records [n, 1152] -> (latent [n,512], rope [n,64]) in fp64 (reading R15).
+    Page "FlashMLA sparse fp8 path gains DCP and MTP", "Related" contrasts the 576-value
+    layout with the packed 656-byte one; "Risks and impact" names the bf16 sparse path."""
+    rec = np.ascontiguousarray(np.asarray(rec, dtype=np.uint8).reshape(-1, BF16_RECORD))
+    v = bf16_to_f64(rec.copy().view("<u2"))
+    return v[:, :LATENT], v[:, LATENT:]
+
+
+RECORD_LAYOUTS = {"fp8_ds_mla": (RECORD, decode_records), "bf16": (BF16_RECORD, decode_records_bf16)}
+
+
 # ----------------------------------------------------------------- index conversion
 
 def convert_index(ids, req, block_table, block_size, dcp_size=1, dcp_rank=0, interleave=1):
@@ -152,7 +170,7 @@ def _gather(cache, slots):
     return np.asarray(cache)[np.asarray(slots, dtype=np.int64)]
 
 
-def attention_rows(q, slots, cache, num_slots, sm_scale):
+def attention_rows(q, slots, cache, num_slots, sm_scale, record_layout="fp8_ds_mla"):
     """Softmax attention of each (row, head) over the row's own candidate records.
 
     Page "FlashMLA sparse fp8 path gains DCP and MTP", "Key source snippets": the
@@ -162,8 +180,9 @@ def attention_rows(q, slots, cache, num_slots, sm_scale):
     out = sum_j exp(s_j - lse) * v_j.  A row with no candidate is (0, -inf)
     (reading R7, same page, "Implementation breakdown" step 3).
 
-    q [T,H,576] float (fp64 arithmetic); slots [T,K]; cache: [num_slots,656] uint8
-    array or an object with ``gather(slots) -> [n,656] bytes``.
+    q [T,H,576] float (fp64 arithmetic); slots [T,K]; cache: [num_slots, record] uint8
+    array or an object with ``gather(slots) -> [n, record] bytes``; ``record_layout``
+    "fp8_ds_mla" (656-byte records) or "bf16" (1152-byte records, reading R15).
     Returns out [T,H,512] fp64, lse [T,H] fp64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -176,7 +195,7 @@ def attention_rows(q, slots, cache, num_slots, sm_scale):
         J = row[(row >= 0) & (row < num_slots)]
         if J.size == 0:
             continue
-        latent, rope = decode_records(_gather(cache, J))
+        latent, rope = RECORD_LAYOUTS[record_layout][1](_gather(cache, J))
         keys = np.concatenate([latent, rope], axis=1)  # [n,576]
         s = sm_scale * (q[t] @ keys.T)  # [H,n]
         m = s.max(axis=1, keepdims=True)
@@ -190,6 +209,11 @@ def attention_rows(q, slots, cache, num_slots, sm_scale):
 def sparse_mla_decode(q, slots, cache, num_slots, sm_scale):
     """Same as :func:`attention_rows`; named after the library call it checks."""
     return attention_rows(q, slots, cache, num_slots, sm_scale)
+
+
+def sparse_mla_decode_bf16(q, slots, cache, num_slots, sm_scale):
+    """:func:`attention_rows` over plain bf16 records (reading R15)."""
+    return attention_rows(q, slots, cache, num_slots, sm_scale, record_layout="bf16")
 
 
 # ----------------------------------------------------------------- DCP merge and layouts

@@ -595,11 +595,45 @@ def test_dense_dcp_merge():
     check_dense_dcp_merge(O.dense_decode, O.merge_lse)
 
 
+# ------------------------------------------------------------------ plain bf16 records
+
+def torch_decode_records_bf16(rec):
+    """Library-based decode of plain bf16 records: torch's bfloat16 view widened to fp64."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8).reshape(-1, 1152)
+    v = torch.from_numpy(rec.copy().view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    return v[:, :512], v[:, 512:]
+
+
+def check_bf16_records_sdpa(decode_bf16, attention):
+    """bf16 records: the decoder against torch's bf16 view, and top-k = every position against
+    scaled_dot_product_attention over the torch-decoded context (fp64, one KV head)."""
+    w = make_random(17, T=3, H=4, K=48, ctx=48, B=16, kv="bf16")
+    assert w.cache.record_bytes == 1152
+    lat, rope = decode_bf16(w.cache.records)
+    tl, tr = torch_decode_records_bf16(w.cache.records)
+    assert np.array_equal(lat, tl) and np.array_equal(rope, tr)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    out, lse = attention(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale, record_layout="bf16")
+    for t in range(w.T):
+        lat, rope = torch_decode_records_bf16(w.cache.gather(_slots_in_order(w.block_table[w.req[t]], 48, 16)))
+        k = torch.from_numpy(np.concatenate([lat, rope], 1))[None, None].expand(1, w.H, 48, 576)
+        v = torch.from_numpy(lat)[None, None].expand(1, w.H, 48, 512)
+        q = torch.from_numpy(w.q_f32()[t].astype(np.float64))[None, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=w.sm_scale)[0, :, 0]
+        ref_lse = torch.logsumexp(w.sm_scale * (q[0, :, 0] @ k[0, 0].T), dim=1)
+        assert np.max(np.abs(out[t] - ref.numpy())) <= 1e-12
+        assert np.max(np.abs(lse[t] - ref_lse.numpy())) <= 1e-12
+
+
+def test_bf16_records_sdpa():
+    check_bf16_records_sdpa(O.decode_records_bf16, O.attention_rows)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 ORIG = {name: getattr(O, name) for name in
         ("decode_records", "e4m3fn_to_f64", "attention_rows", "convert_index", "merge_lse", "e4m3fn_encode",
-         "quantize_records", "cache_write", "dcp_local_seq_lens", "dense_decode")}
+         "quantize_records", "cache_write", "dcp_local_seq_lens", "dense_decode", "decode_records_bf16")}
 
 
 def _mutants():
@@ -617,8 +651,8 @@ def _mutants():
     def sign_flip_e4m3(codes):
         return -ORIG["e4m3fn_to_f64"](codes)
 
-    def lse_without_max(q, slots, cache, n, sc):
-        out, lse = ORIG["attention_rows"](q, slots, cache, n, sc)
+    def lse_without_max(q, slots, cache, n, sc, **kw):
+        out, lse = ORIG["attention_rows"](q, slots, cache, n, sc, **kw)
         return out, lse - 0.5
 
     def convert_swapped_owner(ids, req, bt, B, dcp_size=1, dcp_rank=0, interleave=1):
@@ -634,8 +668,8 @@ def _mutants():
         o, l = ORIG["merge_lse"](outs, lses)
         return np.asarray(outs).sum(axis=0), l
 
-    def qk_transposed_value(q, slots, cache, n, sc):
-        out, lse = ORIG["attention_rows"](q, slots, cache, n, sc)
+    def qk_transposed_value(q, slots, cache, n, sc, **kw):
+        out, lse = ORIG["attention_rows"](q, slots, cache, n, sc, **kw)
         return out[..., ::-1].copy(), lse
 
     def encode_ties_away(x):
@@ -668,7 +702,13 @@ def _mutants():
         perm = np.arange(nb * S).reshape(nb, S).T.reshape(-1)
         return o[perm], l[perm]
 
+    def bf16_rope_first(rec):
+        rec = np.ascontiguousarray(np.asarray(rec, dtype=np.uint8).reshape(-1, 1152))
+        v = O.bf16_to_f64(rec.copy().view("<u2"))
+        return v[:, 64:], v[:, :64]
+
     return {
+        "decode_records_bf16": [bf16_rope_first],
         "dense_decode": [dense_causal_short, dense_rows_s_major],
         "e4m3fn_encode": [encode_ties_away],
         "quantize_records": [quantize_wrong_max, quantize_rope_truncated],
@@ -703,6 +743,7 @@ def _all_pins():
         lambda: check_cache_write_partition(O.cache_write),
         lambda: check_local_seq_lens(O.dcp_local_seq_lens),
         lambda: check_dense_sdpa(O.dense_decode),
+        lambda: check_bf16_records_sdpa(O.decode_records_bf16, O.attention_rows),
         lambda: check_dense_dcp_merge(O.dense_decode, O.merge_lse),
     ]
 

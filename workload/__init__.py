@@ -7,6 +7,7 @@ so that the oracle and the HIP path can both consume it without sharing any of
 the method's arithmetic.
 """
 from .gen import (  # noqa: F401
+    BF16_RECORD_BYTES,
     CONFIGS,
     HEAD_DIM,
     LATENT_DIM,
@@ -20,4 +21,5 @@ from .gen import (  # noqa: F401
     make_dense,
     make_random,
     pack_records,
+    pack_records_bf16,
 )

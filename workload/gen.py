@@ -8,7 +8,8 @@ MTP with DCP2, long-context mixed batch with DCP8).  Every array is drawn from
     global block tables -> shard block tables -> top-k ids -> q -> KV records
 
 fp8_ds_mla record (656 bytes per token; the pages give only the size, 656 vs
-576, so the byte order is this project's own choice):
+576, so the byte order is this project's own choice; ``kv="bf16"`` draws the same
+values into the plain 576-value bf16 layout, 1152 bytes per token, instead):
 
     [0, 512)    512 latent values, OCP e4m3fn codes
     [512, 528)  4 little-endian fp32 scales, scale i covers latent dims 128i..128i+127
@@ -40,6 +41,8 @@ ROPE_DIM = 64
 HEAD_DIM = LATENT_DIM + ROPE_DIM  # 576
 SCALE_TILE = 128
 RECORD_BYTES = LATENT_DIM + 4 * 4 + ROPE_DIM * 2  # 656
+BF16_RECORD_BYTES = 2 * (LATENT_DIM + ROPE_DIM)  # 1152: the plain bf16 layout [latent 512 | rope 64]
+KV_KINDS = {"fp8_ds_mla": RECORD_BYTES, "bf16": BF16_RECORD_BYTES}
 E4M3_MAX = 448.0
 POISON = 0xFF
 
@@ -68,6 +71,16 @@ def pack_records(latent: np.ndarray, rope: np.ndarray) -> np.ndarray:
     return rec
 
 
+def pack_records_bf16(latent: np.ndarray, rope: np.ndarray) -> np.ndarray:
+    """``latent`` [n,512] and ``rope`` [n,64] fp32 -> [n,1152] uint8 records of 576 little-endian bf16
+    (nearest, ties to even): the latent values, then the rope values."""
+    n = np.asarray(latent).shape[0]
+    rec = np.empty((n, BF16_RECORD_BYTES), dtype=np.uint8)
+    rec[:, :2 * LATENT_DIM] = _to_bf16_bits(latent).astype("<u2").view(np.uint8).reshape(n, 2 * LATENT_DIM)
+    rec[:, 2 * LATENT_DIM:] = _to_bf16_bits(rope).astype("<u2").view(np.uint8).reshape(n, 2 * ROPE_DIM)
+    return rec
+
+
 # --------------------------------------------------------------------------- caches
 
 class SparseCache:
@@ -78,6 +91,7 @@ class SparseCache:
     """
 
     def __init__(self, num_slots: int, real_slots: np.ndarray, records: np.ndarray):
+        self.record_bytes = int(records.shape[1])
         order = np.argsort(real_slots, kind="stable")
         self.num_slots = int(num_slots)
         self.real_slots = np.asarray(real_slots, dtype=np.int64)[order]
@@ -89,11 +103,11 @@ class SparseCache:
 
     @property
     def nbytes(self) -> int:
-        return self.num_slots * RECORD_BYTES
+        return self.num_slots * self.record_bytes
 
     def gather(self, slots: np.ndarray) -> np.ndarray:
         slots = np.asarray(slots, dtype=np.int64).reshape(-1)
-        out = np.full((slots.size, RECORD_BYTES), POISON, dtype=np.uint8)
+        out = np.full((slots.size, self.record_bytes), POISON, dtype=np.uint8)
         if self.real_slots.size == 0 or slots.size == 0:
             return out
         pos = np.searchsorted(self.real_slots, slots)
@@ -103,13 +117,13 @@ class SparseCache:
         return out
 
     def dense(self) -> np.ndarray:
-        out = np.full((self.num_slots, RECORD_BYTES), POISON, dtype=np.uint8)
+        out = np.full((self.num_slots, self.record_bytes), POISON, dtype=np.uint8)
         out[self.real_slots] = self.records
         return out
 
     def to_device(self, device) -> torch.Tensor:
-        """Materialise the cache as a [num_slots, 656] uint8 tensor on ``device``."""
-        t = torch.full((self.num_slots, RECORD_BYTES), POISON, dtype=torch.uint8, device=device)
+        """Materialise the cache as a [num_slots, record_bytes] uint8 tensor on ``device``."""
+        t = torch.full((self.num_slots, self.record_bytes), POISON, dtype=torch.uint8, device=device)
         if self.real_slots.size:
             idx = torch.from_numpy(self.real_slots).to(device)
             chunk = 1 << 18
@@ -186,23 +200,25 @@ def _slots_in_order(bt_row: np.ndarray, n_tokens: int, block_size: int) -> np.nd
     return (starts[:, None] + np.arange(block_size, dtype=np.int64)[None, :]).reshape(-1)[:n_tokens]
 
 
-def _draw_records(rng: np.random.Generator, n: int) -> np.ndarray:
-    out = np.empty((n, RECORD_BYTES), dtype=np.uint8)
+def _draw_records(rng: np.random.Generator, n: int, kv: str = "fp8_ds_mla") -> np.ndarray:
+    pack = pack_records if kv == "fp8_ds_mla" else pack_records_bf16
+    out = np.empty((n, KV_KINDS[kv]), dtype=np.uint8)
     step = 1 << 16
     for s in range(0, n, step):
         m = min(step, n - s)
         lat = rng.standard_normal((m, LATENT_DIM), dtype=np.float32)
         rope = rng.standard_normal((m, ROPE_DIM), dtype=np.float32)
-        out[s:s + m] = pack_records(lat, rope)
+        out[s:s + m] = pack(lat, rope)
     return out
 
 
 class _Builder:
     """Accumulates requests, real positions and records, then places them in caches."""
 
-    def __init__(self, block_size: int, dcp_size: int):
+    def __init__(self, block_size: int, dcp_size: int, record_bytes: int = RECORD_BYTES):
         self.B = block_size
         self.D = dcp_size
+        self.rb = record_bytes
 
     def place(self, ctx, real_pos, records_by_req, bt, nphys, shard_bts):
         """Place records (one per real position, per request) in the global and shard caches."""
@@ -229,12 +245,12 @@ class _Builder:
                     s_recs[r].append(recs[ok])
         cat = lambda xs, shape: np.concatenate(xs) if xs else np.zeros(shape, dtype=np.int64)
         gcache = SparseCache(nphys * B, cat(g_slots, (0,)),
-                             np.concatenate(g_recs) if g_recs else np.zeros((0, RECORD_BYTES), np.uint8))
+                             np.concatenate(g_recs) if g_recs else np.zeros((0, self.rb), np.uint8))
         shards = []
         if D > 1:
             for r in range(D):
                 bt_r, nphys_r = shard_bts[r]
-                recs = np.concatenate(s_recs[r]) if s_recs[r] else np.zeros((0, RECORD_BYTES), np.uint8)
+                recs = np.concatenate(s_recs[r]) if s_recs[r] else np.zeros((0, self.rb), np.uint8)
                 shards.append(ShardCache(r, bt_r, SparseCache(max(nphys_r, 1) * B, cat(s_slots[r], (0,)), recs)))
         return gcache, shards
 
@@ -246,9 +262,9 @@ def _distinct(rng, hi: int, k: int) -> np.ndarray:
     return rng.choice(hi, size=k, replace=False).astype(np.int32)
 
 
-def _records_for(rng, real_pos: List[np.ndarray]) -> List[np.ndarray]:
+def _records_for(rng, real_pos: List[np.ndarray], kv: str = "fp8_ds_mla") -> List[np.ndarray]:
     n = sum(int(p.size) for p in real_pos)
-    allrec = _draw_records(rng, n)
+    allrec = _draw_records(rng, n, kv)
     out, off = [], 0
     for p in real_pos:
         out.append(allrec[off:off + p.size])
@@ -269,13 +285,14 @@ CONFIGS: Dict[int, dict] = {
 }
 
 
-def _finish(name, rng, *, H, K, B, D, out_dtype, ids, req, row_pos, ctx, real_pos, bt_pack, shard_bts, note=""):
+def _finish(name, rng, *, H, K, B, D, out_dtype, ids, req, row_pos, ctx, real_pos, bt_pack, shard_bts, note="",
+            kv="fp8_ds_mla"):
     T = ids.shape[0]
     q = rng.standard_normal((T, H, HEAD_DIM), dtype=np.float32)
     q_bits = _to_bf16_bits(q)
-    recs = _records_for(rng, real_pos)
+    recs = _records_for(rng, real_pos, kv)
     bt, nphys = bt_pack
-    cache, shards = _Builder(B, D).place(ctx, real_pos, recs, bt, nphys, shard_bts)
+    cache, shards = _Builder(B, D, KV_KINDS[kv]).place(ctx, real_pos, recs, bt, nphys, shard_bts)
     return Workload(name=name, T=T, H=H, K=K, block_size=B, dcp_size=D, sm_scale=SM_SCALE, out_dtype=out_dtype,
                     q_bits=q_bits, ids=ids.astype(np.int32), req=req.astype(np.int32), row_pos=row_pos.astype(np.int64),
                     ctx=ctx.astype(np.int64), block_table=bt, cache=cache, shards=shards, note=note)
@@ -290,7 +307,7 @@ def _shard_tables(rng, ctx, B, D):
     return out
 
 
-def make_config(cid: int, *, scale_rows: Optional[int] = None) -> Workload:
+def make_config(cid: int, *, scale_rows: Optional[int] = None, kv: str = "fp8_ds_mla") -> Workload:
     """Build benchmark configuration ``cid`` (0..4) with seed 1000 + cid.
 
     ``scale_rows`` (c4 only) keeps the first n decode rows and every k-th prefill row so the
@@ -308,11 +325,11 @@ def make_config(cid: int, *, scale_rows: Optional[int] = None) -> Workload:
         row_pos = np.array([254, 255, 254, 255])
         real = [np.arange(c) for c in ctx]
         return _finish("c0_tiny", rng, H=16, K=64, B=B, D=1, out_dtype="bf16", ids=ids, req=req, row_pos=row_pos,
-                       ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=[])
+                       ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=[], kv=kv)
     if cid == 1:
-        return _make_c1(np.random.Generator(np.random.PCG64(1001)))
+        return _make_c1(np.random.Generator(np.random.PCG64(1001)), kv)
     if cid == 2:
-        return _make_c2()
+        return _make_c2(kv)
     if cid == 3:
         rng = np.random.Generator(np.random.PCG64(1003))
         nreq, ntok, ctxlen, K, D = 64, 4, 32768, 2048, 2
@@ -327,7 +344,7 @@ def make_config(cid: int, *, scale_rows: Optional[int] = None) -> Workload:
             ids[t] = _distinct(rng, int(row_pos[t]) + 1, K)  # causal: ids within [0, pos]
         real = [np.unique(ids[req == b]) for b in range(nreq)]
         return _finish("c3_mtp_dcp2", rng, H=128, K=K, B=B, D=D, out_dtype="bf16", ids=ids, req=req,
-                       row_pos=row_pos, ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts)
+                       row_pos=row_pos, ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts, kv=kv)
     if cid == 4:
         rng = np.random.Generator(np.random.PCG64(1004))
         n_dec, dec_ctx, n_pre, pre_len, K, D = 128, 131072, 2, 2048, 2048, 8
@@ -357,11 +374,11 @@ def make_config(cid: int, *, scale_rows: Optional[int] = None) -> Workload:
             real.append(np.unique(sel[sel >= 0]))
         name = "c4_mixed_dcp8" if scale_rows is None else f"c4_mixed_dcp8_sub{scale_rows}"
         return _finish(name, rng, H=128, K=K, B=B, D=D, out_dtype="bf16", ids=ids, req=req, row_pos=row_pos,
-                       ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts)
+                       ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts, kv=kv)
     raise ValueError(f"unknown config {cid}")
 
 
-def _make_c1(rng) -> Workload:
+def _make_c1(rng, kv: str = "fp8_ds_mla") -> Workload:
     B = 64
     nreq, ctxlen, K = 32, 4096, 2048
     ctx = np.full(nreq, ctxlen, dtype=np.int64)
@@ -371,13 +388,13 @@ def _make_c1(rng) -> Workload:
     row_pos = np.full(nreq, ctxlen - 1)
     real = [np.arange(c) for c in ctx]
     return _finish("c1_decode", rng, H=64, K=K, B=B, D=1, out_dtype="fp32", ids=ids, req=req, row_pos=row_pos,
-                   ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=[])
+                   ctx=ctx, real_pos=real, bt_pack=bt_pack, shard_bts=[], kv=kv)
 
 
-def _make_c2() -> Workload:
+def _make_c2(kv: str = "fp8_ds_mla") -> Workload:
     """c1's 32 rows (identical draws, seed 1001) plus 4 requests of context 2 (seed 1002), DCP4."""
     B, D, K, H = 64, 4, 2048, 64
-    base = _make_c1(np.random.Generator(np.random.PCG64(1001)))
+    base = _make_c1(np.random.Generator(np.random.PCG64(1001)), kv)
     rng = np.random.Generator(np.random.PCG64(1002))
     n_short = 4
     ctx = np.concatenate([base.ctx, np.full(n_short, 2)]).astype(np.int64)
@@ -398,11 +415,12 @@ def _make_c2() -> Workload:
     q_bits = np.concatenate([base.q_bits, q_short])
     # records: c1's real records for its requests, fresh records for the short requests
     short_pos = [np.arange(2) for _ in range(n_short)]
-    short_recs = _records_for(rng, short_pos)
+    short_recs = _records_for(rng, short_pos, kv)
     base_real = [np.arange(c) for c in base.ctx]
     order_slots = [_slots_in_order(base.block_table[b], int(base.ctx[b]), B) for b in range(base.R)]
     base_recs = [base.cache.gather(s) for s in order_slots]
-    cache, shards = _Builder(B, D).place(ctx, base_real + short_pos, base_recs + short_recs, bt, nphys, shard_bts)
+    cache, shards = _Builder(B, D, KV_KINDS[kv]).place(ctx, base_real + short_pos, base_recs + short_recs, bt, nphys,
+                                                       shard_bts)
     return Workload(name="c2_dcp4", T=ids.shape[0], H=H, K=K, block_size=B, dcp_size=D, sm_scale=SM_SCALE,
                     out_dtype="fp32", q_bits=q_bits, ids=ids, req=req.astype(np.int32),
                     row_pos=row_pos.astype(np.int64), ctx=ctx, block_table=bt, cache=cache, shards=shards)
@@ -410,7 +428,7 @@ def _make_c2() -> Workload:
 
 def make_random(seed: int, *, T: int, H: int, K: int, ctx: int, B: int = 64, D: int = 1, n_req: Optional[int] = None,
                 neg_frac: float = 0.0, valid_max: Optional[int] = None, out_dtype: str = "bf16",
-                all_real: bool = True, spare_blocks: int = 0) -> Workload:
+                all_real: bool = True, spare_blocks: int = 0, kv: str = "fp8_ds_mla") -> Workload:
     """Small random workload for parity sweeps: ragged -1 patterns, any H/K/D.
 
     Each row draws ``min(K, ctx)`` distinct ids (or ``valid_max``), scatters them over the K
@@ -437,11 +455,11 @@ def make_random(seed: int, *, T: int, H: int, K: int, ctx: int, B: int = 64, D: 
             sel = ids[req == b]
             real.append(np.unique(sel[sel >= 0]))
     return _finish(f"rand{seed}", rng, H=H, K=K, B=B, D=D, out_dtype=out_dtype, ids=ids, req=req,
-                   row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts)
+                   row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts, kv=kv)
 
 
 def make_dense(seed: int, *, n_req: int, S: int, H: int, ctx, B: int = 64, D: int = 1,
-               out_dtype: str = "bf16") -> Workload:
+               out_dtype: str = "bf16", kv: str = "fp8_ds_mla") -> Workload:
     """Whole-context (dense) decode workload with S query tokens per request (MTP shape).
 
     Request b has context length ctx[b] (an int applies to all); its S query tokens are its
@@ -465,4 +483,4 @@ def make_dense(seed: int, *, n_req: int, S: int, H: int, ctx, B: int = 64, D: in
     real = [np.arange(c) for c in ctxs]
     return _finish(f"dense{seed}", rng, H=H, K=K, B=B, D=D, out_dtype=out_dtype, ids=ids, req=req,
                    row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts,
-                   note=f"dense, S={S}")
+                   note=f"dense, S={S}", kv=kv)
