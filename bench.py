@@ -176,6 +176,78 @@ def main_dense(args):
     print(json.dumps(line), flush=True)
 
 
+def main_bf16(args):
+    """--workload bf16: the top-k decode of the c3 rows (T = 256, H = 128, top-k 2048, context
+    32768) against the unsharded cache in the plain bf16 layout (1152 bytes per token)."""
+    import numpy as np
+    import torch
+    import sparse_mla_decode_topk_amd as smla
+    from workload import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    smla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log("generating workload c3 with bf16 records (T=256, H=128, top-k 2048, ctx 32768) ...")
+    w = make_config(3, kv="bf16")
+    q = w.q_torch().to(dev)
+    caches = [w.cache.to_device(dev) for _ in range(max(1, args.replicas))]
+    bt = torch.from_numpy(w.block_table).to(dev)
+    slots, _ = smla.convert_index(torch.from_numpy(w.ids).to(dev), torch.from_numpy(w.req).to(dev), bt, w.block_size)
+    out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(i):
+        smla.decode(q, caches[i % len(caches)], slots, w.sm_scale, out=out, lse=lse, kv_layout="bf16")
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        run(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    nvalid = int((w.ids >= 0).sum())
+    byts = 1152 * nvalid + w.T * w.H * 576 * 2 + w.T * w.K * 4 + w.T * w.H * (512 * 2 + 4)
+    flops = FLOP_PER_VALID_ID_PER_HEAD * w.H * nvalid
+    roof = roofline_entry(byts, flops, call_s)
+    roof.update({"traffic": None, "kernel": "decode_bf16_kernel (one unsharded call)", "launch_us": round(call_s * 1e6, 2),
+                 "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
+                 "mfma_frac": round(flops / call_s / (BF16_PEAK_TFLOPS * 1e12), 4)})
+    line = {
+        "metric": METRIC, "value": round(w.T * args.steps / wall, 1), "unit": "query-rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "c3_bf16kv: 64 req x 4 MTP tokens (T=256), H=128, top-k 2048 causal, ctx 32768, "
+                               "plain bf16 cache (1152 B/token), unsharded", "T": w.T, "H": w.H, "topk": w.K,
+                   "ctx": 32768, "block_size": w.block_size, "cache_replicas": len(caches)},
+        "kv_gbps": round(1152 * nvalid / call_s / 1e9, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.smla_oracle as O
+        log("timing the CPU oracle on a bounded sample ...")
+        rows_done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_budget:
+            sub = w.rows([rows_done % w.T])
+            sl, _ = O.convert_index(sub.ids, sub.req, sub.block_table, sub.block_size)
+            O.attention_rows(sub.q_f32(), sl, sub.cache, sub.cache.num_slots, sub.sm_scale, record_layout="bf16")
+            rows_done += 1
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(rows_done / el, 3), "unit": "query-rows/s", "cores": blas_threads(),
+                                "kind": "oracle",
+                                "sample": f"{rows_done} rows of the same workload in order through the fp64 numpy "
+                                          f"oracle (conversion and attention over bf16 records); {el:.1f} s on "
+                                          f"{blas_threads()} host CPUs"}
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(w, budget_s):
     """fp64 oracle of the same DCP2 step (converts, shard attention, merge) over the rows in
     order, wrapping around, until the time budget is spent; rows/s over the rows done."""
@@ -242,8 +314,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unsharded", action="store_true",
                     help="also time the unsharded decode of the same rows (reported beside the step)")
-    ap.add_argument("--workload", choices=("c3", "dense"), default="c3",
-                    help="c3: the DCP2 MTP step (default); dense: the whole-context MTP decode")
+    ap.add_argument("--workload", choices=("c3", "dense", "bf16"), default="c3",
+                    help="c3: the DCP2 MTP step (default); dense: the whole-context MTP decode; bf16: the c3 rows "
+                         "unsharded against a plain bf16 cache")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -253,6 +326,9 @@ def main():
         sys.exit(2)
     if args.workload == "dense":
         main_dense(args)
+        return
+    if args.workload == "bf16":
+        main_bf16(args)
         return
 
     import numpy as np

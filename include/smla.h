@@ -151,6 +151,26 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
                       int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sparse_mla_decode_bf16 - sparse_mla_decode over a plain bf16 latent cache instead of the
+ * packed fp8_ds_mla one.
+ *
+ * [P-FlashMLA] "Related" (the 576-value layout against the 656-byte packed one) and
+ * "Risks and impact" (the bf16 sparse path, which the pages' serving stack keeps out of
+ * its DCP support; here every call works the same for both layouts).
+ *
+ * kv_cache  [num_slots, 1152] bytes, 16-byte aligned: record s = 576 little-endian bf16
+ *           values at kv_cache + 1152*s, the 512 latent values then the 64 rope values;
+ *           key = all 576, value = the 512 latent values.
+ * Every other argument, the workspace (sparse_mla_decode_workspace_size), the result and
+ * the errors are those of sparse_mla_decode.
+ */
+int sparse_mla_decode_bf16(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                           int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
+                           int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
+                           int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * sparse_mla_merge_lse - combine S partial results over disjoint KV shards.
  *
  * [P-FlashMLA] "Implementation breakdown" steps 1 and 3 (the shared DCP merge

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     sparse_mla_convert_index,
     sparse_mla_dcp_local_seq_lens,
     sparse_mla_decode,
+    sparse_mla_decode_bf16,
     sparse_mla_decode_workspace_size,
     sparse_mla_dense_decode,
     sparse_mla_dense_decode_workspace_size,

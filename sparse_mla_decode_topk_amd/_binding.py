@@ -62,6 +62,8 @@ def load_library():
         lib.sparse_mla_decode.restype = ctypes.c_int
         lib.sparse_mla_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _F32, _P, _I32, _I64,
                                           _I64, _P, _I64, _I64, _I32, _P, _SZ, _P]
+        lib.sparse_mla_decode_bf16.restype = ctypes.c_int
+        lib.sparse_mla_decode_bf16.argtypes = lib.sparse_mla_decode.argtypes
         lib.sparse_mla_merge_lse.restype = ctypes.c_int
         lib.sparse_mla_merge_lse.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I32,
                                              _I64, _I64, _P, _I64, _I64, _P]
@@ -138,6 +140,10 @@ def sparse_mla_decode(*args) -> int:
     return load_library().sparse_mla_decode(*args)
 
 
+def sparse_mla_decode_bf16(*args) -> int:
+    return load_library().sparse_mla_decode_bf16(*args)
+
+
 def sparse_mla_merge_lse(*args) -> int:
     return load_library().sparse_mla_merge_lse(*args)
 
@@ -210,11 +216,15 @@ def convert_index(topk_ids: torch.Tensor, req_id_per_token: torch.Tensor, block_
     return out, valid
 
 
+KV_LAYOUTS = {"fp8_ds_mla": RECORD_BYTES, "bf16": 2 * HEAD_DIM}
+
+
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax_scale: float,
            out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
            lse: Optional[torch.Tensor] = None, lse_layout: str = "TH", num_splits: int = 0,
-           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Sparse MLA decode.  q [T,H,576] bf16, kv_cache [num_slots,656] uint8, slots [T,K] int32.
+           workspace: Optional[torch.Tensor] = None, kv_layout: str = "fp8_ds_mla") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse MLA decode.  q [T,H,576] bf16, kv_cache [num_slots,656] uint8 (kv_layout "fp8_ds_mla")
+    or [num_slots,1152] (kv_layout "bf16": 576 bf16 values per token), slots [T,K] int32.
 
     Returns out [T,H,512] (out_dtype) and lse.  lse_layout "TH" gives a [T,H] tensor;
     "HT" writes the kernel-native [H,T] layout and returns its [T,H] transposed view.
@@ -225,8 +235,11 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax
     T, H, D = q.shape
     if D != HEAD_DIM or q.stride(2) != 1:
         raise ValueError("q must be [T,H,576] with contiguous dims")
-    if kv_cache.shape[1] != RECORD_BYTES or not kv_cache.is_contiguous():
-        raise ValueError("kv_cache must be a contiguous [num_slots,656] uint8 tensor")
+    if kv_layout not in KV_LAYOUTS:
+        raise ValueError(f"kv_layout must be one of {sorted(KV_LAYOUTS)}")
+    rb = KV_LAYOUTS[kv_layout]
+    if kv_cache.shape[1] != rb or not kv_cache.is_contiguous():
+        raise ValueError(f"kv_cache must be a contiguous [num_slots,{rb}] uint8 tensor")
     K = slots.shape[1]
     if slots.shape[0] != T or (K > 1 and slots.stride(1) != 1):
         raise ValueError("slots must be [T,K] with a contiguous last dimension")
@@ -253,11 +266,12 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax
     if ws_ptr is not None and ws_ptr % 256:
         pad = (-ws_ptr) % 256
         ws_ptr, ws_bytes = ws_ptr + pad, ws_bytes - pad
-    st = sparse_mla_decode(
+    call = sparse_mla_decode if kv_layout == "fp8_ds_mla" else sparse_mla_decode_bf16
+    st = call(
         q.data_ptr(), _st(q, 0), _st(q, 1), kv_cache.data_ptr(), kv_cache.shape[0], slots.data_ptr(),
         _st(slots, 0), T, H, K, float(softmax_scale), out.data_ptr(), _dtype_code(out.dtype), _st(out, 0),
         _st(out, 1), lse.data_ptr(), _st(lse, 0), _st(lse, 1), num_splits, ws_ptr, ws_bytes, _stream(dev))
-    _check("sparse_mla_decode", st)
+    _check(call.__name__, st)
     return out, lse
 
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsmla.so")
-SOURCES = ["smla_api.hip", "convert_index.hip", "decode.hip", "merge_lse.hip", "cache_write.hip", "dense_slots.hip"]
+SOURCES = ["smla_api.hip", "convert_index.hip", "decode.hip", "merge_lse.hip", "cache_write.hip", "dense_slots.hip", "decode_bf16.hip"]
 ARCH = os.environ.get("SMLA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -43,29 +43,15 @@
 //    scope counter, zeroed by a small kernel before the decode kernel) merges them.
 //  * A row with no valid entry yields out = 0, lse = -inf.
 
-#include "smla_internal.h"
-
-#include <math.h>
+#include "decode_common.h"
 
 namespace smla {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(8))) int i32x8;
-typedef __attribute__((ext_vector_type(4))) int i32x4;
-typedef __attribute__((ext_vector_type(2))) int i32x2;
-#define SMLA_LDS __attribute__((address_space(3)))
+using namespace dec;
 
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRefHeadroom = 64.0f;  // log2 units a score may exceed the reference by
 constexpr int kUnitScale = 127;       // E8M0 encoding of 2^0 for the scaled fp8 MFMA
 
-constexpr int kThreads = 512;                   // 4 score waves + 4 value waves
 constexpr int kTT = 32;                         // records per tile
 constexpr int kChunks = kRecordBytes / 16;      // 41 chunks of 16 bytes per record
 constexpr int kCS = 16 * kTT;                   // bytes per chunk row of a tile
@@ -73,7 +59,6 @@ constexpr int kTileBytes = kChunks * kCS;       // 20992
 constexpr int kStages = 4;                      // tile buffers: scores on n, values on n-1,
 constexpr int kAhead = kStages - 2;             //   loads in flight for n+1 .. n+kAhead
 constexpr int kLoads = (kChunks + 1) / 2;       // 21 global_load_lds per tile, two chunks each
-constexpr int kHB = kHeadsPerBlock;             // 64 heads per workgroup
 constexpr int kPRow = 2 * kTT;                  // bytes per head row of a probability tile
 constexpr int kPTile = kHB * kPRow;             // one scale tile of probabilities (4 KB)
 constexpr int kPBuf = 4 * kPTile;               // all four scale tiles (16 KB)
@@ -102,18 +87,8 @@ __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 __device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
-}
-
-__device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Four fp32 values -> packed e4m3 hi terms and the exact residual lo terms.
@@ -126,24 +101,6 @@ __device__ __forceinline__ void split_e4m3(float x0, float x1, float x2, float x
   l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b23[0], x3 - b23[1], l, true);
   hi = h;
   lo = l;
-}
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also orders global memory, which
-// makes every wave drain its in-flight HBM -> LDS copies at each barrier; the copies are
-// instead waited for explicitly (wait_tile) by the waves that issued them.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// max of a value over lanes l, l^16, l^32, l^48 (every lane gets it), on the VALU
-__device__ __forceinline__ float max4x16(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Global->LDS loads one value wave issues per tile: load j of a tile belongs to wave j % 4.
@@ -160,17 +117,6 @@ __device__ __forceinline__ void wait_tile(int tiles_newer, int b) {
     case 12: wait_vmcnt<12>(); break;
     default: wait_vmcnt<0>(); break;
   }
-}
-
-// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes land at
-// LDS address lds + 16 i.  Issued as inline assembly so the compiler does not treat every
-// later LDS read as a possible alias of the copy and drain all copies in flight before it;
-// the waves wait for their own copies explicitly (wait_tile) before the barrier that
-// publishes a tile.  M0 (the LDS base of the copy) is written right before each copy; the
-// kernel has no other M0 user.
-__device__ __forceinline__ void lds_dma16(const uint8_t* src, const uint8_t* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(SMLA_LDS void*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
 // HBM -> LDS copy of one tile by value wave b (0..3): load j moves chunks 2j and 2j+1 of all
@@ -191,10 +137,6 @@ __device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, con
   const int idx = min(n * kTT + (lane & 31), total - 1);
   return p.kv + (int64_t)sh.clist[idx] * kRecordBytes + 16 * (lane >> 5);
 }
-
-struct Block {
-  int row, hb, split, h_lo, nh, total, ntiles;
-};
 
 // ---------------------------------------------------------------------------------------
 // Score wave `sw` (0..3): heads h_lo + 16sw + (lane & 15); lane group g = lane >> 4 holds
@@ -470,132 +412,16 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
   }
 }
 
-// The last split of a (row, head block) to arrive merges every split's partial.  First one
-// thread per head turns the splits' (max, sum) into normalised weights in LDS (and writes the
-// head's LSE); then each thread owns 4 dims of every fourth head and, split by split, loads
-// all of its partial rows before accumulating them, so the merge costs one memory round trip
-// per split rather than several per output element.
-__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, Shared& sh, int tid) {
-  float* wts = reinterpret_cast<float*>(sh.stage);  // [head][split]; the tile buffers are free now
-  if (tid < bk.nh) {
-    const int h = bk.h_lo + tid;
-    const float* ml = p.ws_ml + ((int64_t)bk.row * p.splits * p.H + h) * 2;  // split sp at + sp * H * 2
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2));
-    float L = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int sp = 0; sp < p.splits; ++sp) {
-        const float ms = __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2);
-        const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
-        wts[tid * p.splits + sp] = w;
-        L += w * __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2 + 1);
-      }
-    }
-    const bool empty = !(L > 0.0f);
-    const float inv = empty ? 0.0f : 1.0f / L;
-    for (int sp = 0; sp < p.splits; ++sp) wts[tid * p.splits + sp] = empty ? 0.0f : wts[tid * p.splits + sp] * inv;
-    p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
-  }
-  __syncthreads();
-  constexpr int kPerThread = kHB * (kLatent / 4) / kThreads;  // 16 (head, 4-dim) items per thread
-  const int d4 = tid % (kLatent / 4);
-  const int h0 = tid / (kLatent / 4);  // heads h0, h0 + 4, ... (wave-uniform)
-  f32x4 acc[kPerThread];
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < p.splits; ++sp) {
-    f32x4 part[kPerThread];
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int hl = h0 + (kThreads / (kLatent / 4)) * i;
-      part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (hl < bk.nh && wts[hl * p.splits + sp] != 0.0f) {
-        const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + bk.h_lo + hl;
-        part[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int hl = h0 + (kThreads / (kLatent / 4)) * i;
-      if (hl < bk.nh) acc[i] += wts[hl * p.splits + sp] * part[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int hl = h0 + (kThreads / (kLatent / 4)) * i;
-    if (hl >= bk.nh) continue;
-    const int h = bk.h_lo + hl;
-    if (p.out_fp32) {
-      float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc[i];
-    } else {
-      __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<bf16x4*>(orow + 4 * d4) =
-          bf16x4{(__bf16)acc[i][0], (__bf16)acc[i][1], (__bf16)acc[i][2], (__bf16)acc[i][3]};
-    }
-  }
-}
-
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) Shared sh;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
 
-  // Consecutive blocks are dispatched round-robin over the 8 XCDs; give every XCD a
-  // contiguous range of work items so the head blocks and splits of a row run side by side
-  // on one XCD and share its L2.
-  const int per_xcd = (int)((gridDim.x + 7) / 8);
-  const int wg = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (wg >= p.T * p.head_blocks * p.splits) return;
   Block bk;
-  bk.split = wg % p.splits;
-  const int rest = wg / p.splits;
-  bk.hb = rest % p.head_blocks;
-  bk.row = rest / p.head_blocks;
-  bk.h_lo = bk.hb * kHB;
-  bk.nh = min(kHB, p.H - bk.h_lo);  // a multiple of 16
-
-  // ---- compact this split's slot entries (valid = within [0, num_slots))
-  const int e0 = bk.split * p.entries_per_split;
-  const int e1 = min(p.K, e0 + p.entries_per_split);
-  const int32_t* srow = p.slots + (int64_t)bk.row * p.slots_ld;
-  int total = 0;
-  for (int base = e0; base < e1; base += kThreads * 4) {
-    int vals[4];
-    int wcount = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = base + i * kThreads + tid;
-      const int v = e < e1 ? srow[e] : -1;
-      const bool ok = v >= 0 && (int64_t)v < p.num_slots;
-      vals[i] = ok ? v : -1;
-      wcount += __popcll(__ballot(ok));
-    }
-    if (lane == 0) sh.wave_cnt[wave] = wcount;
-    __syncthreads();
-    int off = total, all = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-      const int c = sh.wave_cnt[w];
-      off += w < wave ? c : 0;
-      all += c;
-    }
-    const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = vals[i] >= 0;
-      const unsigned long long bm = __ballot(ok);
-      if (ok) sh.clist[off + __popcll(bm & below)] = vals[i];
-      off += __popcll(bm);
-    }
-    total += all;
-    __syncthreads();
-  }
-  bk.total = total;
-  bk.ntiles = (total + kTT - 1) / kTT;
+  if (!block_of(p, bk)) return;
+  bk.total = compact_slots(p, bk, sh, tid, wave, lane);
+  bk.ntiles = (bk.total + kTT - 1) / kTT;
 
   // The two roles run the same number of workgroup barriers, one per loop step.
   if (wave < 4)
@@ -604,20 +430,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     value_role(p, sh, bk, wave - 4, lane);
   if (p.splits == 1) return;
 
-  // ---- split-K: the last split of this (row, head block) to arrive combines all of them.
-  // The barrier completes every wave's partial stores; one device-scope acquire-release
-  // atomic by one thread then publishes them and, in the last split, makes the other splits'
-  // partials visible to the workgroup after the second barrier.  (A device-scope fence in
-  // every thread would make each wave write back the L2 of its XCD: measured twice as slow.)
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.ws_cnt + (int64_t)bk.row * p.head_blocks + bk.hb, 1, __ATOMIC_ACQ_REL,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    sh.last_flag = old == p.splits - 1;
-  }
-  __syncthreads();
-  if (!sh.last_flag) return;
-  combine_splits(p, bk, sh, tid);
+  if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, tid);
+
 }
 
 __global__ void zero_counters(int32_t* cnt, int64_t n) {

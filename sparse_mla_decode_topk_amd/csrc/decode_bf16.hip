@@ -1,0 +1,318 @@
+// Sparse MLA decode over per-row top-k slot lists against a plain bf16 latent cache: 576
+// little-endian bf16 values per token (512 latent, then 64 rope; 1152 bytes), the layout
+// page "FlashMLA sparse fp8 path gains DCP and MTP" contrasts with the packed fp8_ds_mla one
+// ("Related": 576 against 656; "Risks and impact": the bf16 sparse path).  Same contract as
+// the fp8 decode: out[t,h,0:512] and lse[t,h] of softmax attention over the row's own
+// candidate records, (0, -inf) for a row without one, split-K with an in-kernel merge.
+//
+// gfx950 design (the fp8 kernel's structure, without scales, query split or widening)
+//  * A workgroup owns one row, up to 64 heads and one range of the row's top-k list: four
+//    score waves (16 heads each) and four value waves (128 output dims each), one of each
+//    per SIMD.
+//  * Tiles of 16 records, copied HBM -> LDS by the value waves with global_load_lds_dwordx4
+//    four tiles ahead (6 tile buffers): one copy moves four 16-byte chunks of the 16 records,
+//    so a tile sits chunk-major in LDS ([72 chunks][16 records][16 B]).
+//  * QK^T on v_mfma_f32_16x16x32_bf16 over all 576 dims (18 k-steps, two accumulators):
+//    the record's bf16 values are the operand as stored, q stays in registers as bf16, and
+//    scores come out as S^T (tokens x heads), one head per lane.  No per-tile scale.
+//  * Softmax in base 2 against a per-head reference max fixed at the first tile (a second
+//    pass with the exact max if a score ever exceeds it by more than 2^64), so the output
+//    accumulators are never rescaled; P = bf16(p) goes to LDS once per tile as
+//    [head][token] rows padded to 48 bytes (conflict-free reads).
+//  * PV on v_mfma_f32_32x32x16_bf16: O^T[dim, head] += V^T[dim, token] . P^T[token, head];
+//    the V^T operand comes straight from the staged tile through two ds_read_b64_tr_b16 per
+//    32-dim block (lane i of a 16-lane group receives dim D0 + i of four consecutive tokens).
+//  * One LDS-only barrier per tile; split-K arrival and merge as in the fp8 kernel.
+
+#include "decode_common.h"
+
+namespace smla {
+namespace {
+
+using namespace dec;
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+constexpr int kRecB = 2 * kHeadDim;          // 1152 bytes per record
+constexpr int kTT = 16;                      // records per tile
+constexpr int kChunks = kRecB / 16;          // 72 chunks of 16 bytes per record
+constexpr int kCS = 16 * kTT;                // 256 bytes per chunk row of a tile
+constexpr int kTileBytes = kChunks * kCS;    // 18432
+constexpr int kStages = 6;                   // tile buffers: scores on n, values on n-1,
+constexpr int kAhead = kStages - 2;          //   loads in flight for n+1 .. n+kAhead
+constexpr int kLoads = kChunks / 4;          // 18 global_load_lds per tile, four chunks each
+constexpr int kKSteps = kHeadDim / 32;       // 18 QK k-steps of 32 dims
+constexpr int kPRow = 48;                    // bytes per head row of a probability tile (32 used)
+constexpr int kPTile = kHB * kPRow;          // 3 KB
+
+static_assert(kRecB % 64 == 0, "a copy moves four whole chunks");
+static_assert(kAhead == 4, "load waits below are written for 4 tiles ahead");
+static_assert(kHB * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile buffers");
+
+struct Shared {
+  uint8_t stage[kStages * kTileBytes];
+  uint8_t pbuf[2 * kPTile];
+  int32_t clist[kMaxEntriesPerSplit];
+  float ml[2 * kHB];  // per head of the block: (reference max, sum)
+  int32_t wave_cnt[kThreads / 64];
+  int32_t last_flag;
+};
+
+// Copies value wave b issues per tile: copy j of a tile belongs to wave j % 4.
+__device__ __forceinline__ int loads_of_wave(int b) { return b < kLoads % 4 ? kLoads / 4 + 1 : kLoads / 4; }
+
+// Wait until this wave's copies of tile n have landed, given `tiles_newer` later tiles of
+// this wave still in flight (wave-uniform).
+__device__ __forceinline__ void wait_tile(int tiles_newer, int b) {
+  switch (tiles_newer * loads_of_wave(b)) {
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// HBM -> LDS copy of one tile by value wave b (0..3): copy j moves chunks 4j .. 4j+3 of all
+// 16 records (lane l: record l % 16, chunk 4j + l / 16) into the contiguous kilobyte j of the
+// chunk-major tile.  `rec` is this lane's record plus 16 (l / 16) bytes.
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, int b) {
+#pragma unroll
+  for (int k = 0; k < (kLoads + 3) / 4; ++k) {
+    const int j = b + 4 * k;
+    if (j < kLoads) lds_dma16(rec + 64 * j, stage + 1024 * j);
+  }
+}
+
+// Record of tile entry (lane % 16); entries past the end of the list repeat the last one.
+__device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, const Shared& sh, int n, int total,
+                                                      int lane) {
+  const int idx = min(n * kTT + (lane & 15), total - 1);
+  return p.kv + (int64_t)sh.clist[idx] * kRecB + 16 * (lane >> 4);
+}
+
+// ---------------------------------------------------------------------------------------
+// Score wave `sw` (0..3): heads h_lo + 16sw + (lane & 15); lane group g = lane >> 4 holds
+// the query dims 32ks + 8g .. +7 of every k-step ks.
+__device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, const Block& bk, int sw, int lane) {
+  const int g = lane >> 4;
+  const int hl = 16 * sw + (lane & 15);  // head within the block
+  const bool active = 16 * sw < bk.nh;
+  bf16x8 qv[kKSteps];
+  if (active) {
+    const uint16_t* qp = p.q + (int64_t)bk.row * p.q_st + (int64_t)(bk.h_lo + hl) * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qv[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * g);
+  } else {
+    // an idle score wave (fewer than 64 heads) keeps its probability rows at zero
+    for (int i = lane; i < 2 * 16 * (kPRow / 16); i += 64) {
+      const int seg = i % (kPRow / 16), r = (i / (kPRow / 16)) % 16, tb = i / (16 * (kPRow / 16));
+      *reinterpret_cast<i32x4*>(sh.pbuf + tb * kPTile + (16 * sw + r) * kPRow + 16 * seg) = i32x4{0, 0, 0, 0};
+    }
+  }
+  const float cq = p.scale_log2;
+
+  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.0f;  // per head, same in its four lanes
+  for (int pass = 0; pass < 2; ++pass) {
+    bool over = false;  // a score exceeded the reference by more than the headroom
+    for (int n = 0; n <= bk.ntiles; ++n) {
+      lds_barrier();  // tile n staged; P(n-2) consumed by the value waves
+      if (!active || n >= bk.ntiles) continue;
+      // ---- S^T for tile n: lane holds head hl, tokens 4g + r
+      const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
+      const int nin = min(kTT, bk.total - n * kTT);
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));  // recompute lane-derived addresses here instead of hoisting them
+      const uint8_t* kr = tile + 16 * (lane_o & 15) + (lane_o >> 4) * kCS;
+      f32x4 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ks += 2) {
+        acc0 = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + 4 * ks * kCS), qv[ks], acc0);
+        acc1 = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + 4 * (ks + 1) * kCS), qv[ks + 1], acc1);
+      }
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = (acc0[r] + acc1[r]) * cq;
+      if (nin < kTT) {  // tail tile: entries past the end of the list get p = 0
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r >= nin) pv[r] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3]));
+      mx = max4x16(mx);
+      m_max = fmaxf(m_max, mx);
+      m_ref = m_ref == -INFINITY ? mx : m_ref;
+      over |= mx > m_ref + kRefHeadroom;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = fast_exp2(pv[r] - m_ref);
+        lsum += pv[r];
+      }
+      l_run += lsum;
+      // P = bf16(p) as [head][token]: this lane's tokens 4g .. 4g+3 of head hl
+      *reinterpret_cast<bf16x4*>(sh.pbuf + (n & 1) * kPTile + hl * kPRow + 8 * g) =
+          bf16x4{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+    }
+    // a second pass, with the exact max as reference, only if some score outgrew the headroom
+    if (!__syncthreads_or(over)) break;
+    m_ref = m_max;
+    l_run = 0.0f;
+  }
+
+  // ---- per-head (max, sum) for the value waves; lse or the split partial
+  if (active) {
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const float mo = l_tot > 0.0f ? m_ref : -INFINITY;
+    if (g == 0) {
+      sh.ml[2 * hl] = mo;
+      sh.ml[2 * hl + 1] = l_tot;
+      const int head = bk.h_lo + hl;
+      if (p.splits == 1) {
+        p.lse[(int64_t)bk.row * p.l_st + (int64_t)head * p.l_sh] =
+            l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t pidx = ((int64_t)bk.row * p.splits + bk.split) * p.H + head;
+        p.ws_ml[pidx * 2 + 0] = mo;
+        p.ws_ml[pidx * 2 + 1] = l_tot;
+      }
+    }
+  }
+  __syncthreads();  // sums visible to the value waves
+}
+
+// ---------------------------------------------------------------------------------------
+// Value wave `vw` (0..3): output dims 128vw .. +127 of every head of the block; also the
+// loader of the tiles.
+__device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, const Block& bk, int vw, int lane) {
+  // O^T blocks o[db][hg]: dims 128vw + 32db + 8(r/4) + 4(lane/32) + r%4, head 32hg + lane%32
+  f32x16 o[4][2];
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) o[db][hg] = f32x16{};
+    for (int n = 0; n < kAhead && n < bk.ntiles; ++n)
+      issue_tile(sh.stage + n * kTileBytes, lane_record(p, sh, n, bk.total, lane), vw);
+    for (int n = 0; n <= bk.ntiles; ++n) {
+      wait_tile(min(kAhead - 1, max(bk.ntiles - 1 - n, 0)), vw);  // tile n is in
+      lds_barrier();  // tile n staged; P(n-1) written; tile n-2 and P(n-2) consumed
+      if (n + kAhead < bk.ntiles)
+        issue_tile(sh.stage + ((n + kAhead) % kStages) * kTileBytes, lane_record(p, sh, n + kAhead, bk.total, lane),
+                   vw);
+      if (n == 0) continue;
+      // ---- O^T += V^T P^T for tile n-1 (tokens past the end carry P = 0 against real records)
+      const int m = n - 1;
+      const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
+      const uint8_t* pb = sh.pbuf + (m & 1) * kPTile;
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int h32 = lane_o & 31, lh = lane_o >> 5;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) pf[hg] = *reinterpret_cast<const bf16x8*>(pb + (32 * hg + h32) * kPRow + 16 * lh);
+      // tr16 source of this lane a (in its 16-lane group G = lane / 16): token 8(G/2) + a/4 (+4 for
+      // the second read), dims D0 + 4(a%4) .. +3 with D0 = 128vw + 32db + 16(G%2)
+      const int a = lane_o & 15, G = lane_o >> 4;
+      const int dl = 16 * (G & 1) + 4 * (a & 3);  // dim within the 32-dim block, a multiple of 4
+      const uint8_t* vsrc = tile + 16 * (8 * (G >> 1) + (a >> 2)) + 2 * (dl & 7) + (dl >> 3) * kCS;
+      bf16x8 va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* base = vsrc + (4 * (4 * vw + db)) * kCS;  // chunk of dim 128vw + 32db
+        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS i16x4*)(base));
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS i16x4*)(base + 4 * 16));
+        va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int hg = 0; hg < 2; ++hg) o[db][hg] = mfma32_bf16(va[db], pf[hg], o[db][hg]);
+    }
+    if (!__syncthreads_or(false)) break;
+  }
+  __syncthreads();  // the score waves' (max, sum) are in LDS
+
+  const int h32 = lane & 31;
+  const int dbase = 128 * vw + 4 * (lane >> 5);  // + 32db + 8qd
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    const int hl = 32 * hg + h32;
+    if (hl >= bk.nh) continue;
+    const int head = bk.h_lo + hl;
+    if (p.splits == 1) {
+      const float lt = sh.ml[2 * hl + 1];
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      if (p.out_fp32) {
+        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd) =
+                f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
+      } else {
+        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * qd) =
+                bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
+                       (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
+      }
+    } else {
+      // split-K: this split's unnormalised partial
+      float* po = p.ws_o + (((int64_t)bk.row * p.splits + bk.split) * p.H + head) * kLatent + dbase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd) =
+              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]};
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) Shared sh;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+  const int lane = tid & 63;
+  Block bk;
+  if (!block_of(p, bk)) return;
+  bk.total = compact_slots(p, bk, sh, tid, wave, lane);
+  bk.ntiles = (bk.total + kTT - 1) / kTT;
+
+  // The two roles run the same number of workgroup barriers, one per loop step.
+  if (wave < 4)
+    score_role(p, sh, bk, wave, lane);
+  else
+    value_role(p, sh, bk, wave - 4, lane);
+  if (p.splits == 1) return;
+  if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, tid);
+}
+
+__global__ void zero_counters_bf16(int32_t* cnt, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) cnt[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
+  const int64_t items = (int64_t)p.T * plan.head_blocks * plan.splits;
+  const unsigned grid = (unsigned)((items + 7) / 8 * 8);
+  if (plan.splits > 1) {
+    // arrival counters start at zero on every call (a kernel, not a memset node)
+    const int64_t n = (int64_t)p.T * plan.head_blocks;
+    hipLaunchKernelGGL(zero_counters_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.ws_cnt, n);
+  }
+  hipLaunchKernelGGL(decode_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -210,6 +210,20 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
   return launch_decode(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
+int sparse_mla_decode_bf16(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                           int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
+                           int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
+                           int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DecodeParams p;
+  DecodePlan plan;
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, T, H, K,
+                                softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse, lse_stride_t,
+                                lse_stride_h, num_splits, workspace, workspace_bytes, p, plan);
+  if (st != SMLA_OK || T == 0) return st;
+  return launch_decode_bf16(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
 size_t sparse_mla_dense_decode_workspace_size(int32_t B, int32_t S, int32_t H, int32_t max_seq_len,
                                               int32_t dcp_size, int32_t interleave) {
   if (B <= 0 || S < 1 || H < 1 || max_seq_len < 0 || dcp_size < 1 || interleave < 1) return 0;

@@ -99,6 +99,7 @@ struct DecodePlan {
 
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_dense_slots(const DenseSlotParams& p, hipStream_t stream);

@@ -31,7 +31,7 @@ def test_header_lists_the_calls():
     names = declared_functions()
     for n in ("smla_abi_version", "smla_status_string", "sparse_mla_convert_index", "sparse_mla_decode",
               "sparse_mla_decode_workspace_size", "sparse_mla_merge_lse", "sparse_mla_cache_write",
-              "sparse_mla_dcp_local_seq_lens", "sparse_mla_dense_decode", "sparse_mla_dense_decode_workspace_size"):
+              "sparse_mla_dcp_local_seq_lens", "sparse_mla_dense_decode", "sparse_mla_dense_decode_workspace_size", "sparse_mla_decode_bf16"):
         assert n in names
 
 
@@ -104,6 +104,13 @@ def decode_call(lib, **kw):
 ])
 def test_decode_validation(lib, kw, want):
     assert decode_call(lib, **kw) == want
+    # the bf16-record decode validates its arguments the same way
+    a = dict(q=A16, qst=128 * 576, qsh=576, kv=A16, ns=100, slots=A16, sld=64, T=2, H=128, K=64, scale=0.07,
+             out=A16, odt=0, ost=128 * 512, osh=512, lse=A16, lst=128, lsh=1, splits=0, ws=None, wsb=0)
+    a.update(kw)
+    assert lib.sparse_mla_decode_bf16(a["q"], a["qst"], a["qsh"], a["kv"], a["ns"], a["slots"], a["sld"], a["T"],
+                                      a["H"], a["K"], a["scale"], a["out"], a["odt"], a["ost"], a["osh"], a["lse"],
+                                      a["lst"], a["lsh"], a["splits"], a["ws"], a["wsb"], None) == want
 
 
 def test_workspace_size(lib):
