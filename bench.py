@@ -283,9 +283,10 @@ def cpu_baseline(w, budget_s):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "d239eb26099fa8559844d93e673055858e91d13d729c4ef56e11bd1ea6d97ece",
-                  "fetch_bytes": 227312368, "write_bytes": 67247644}
-KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
+DECODE_TRAFFIC = {"sources_sha256": "1535cfdd97bcf6dc747d55b08d2708011554bc2508da84ae54836302aba4c6ac",
+                  "fetch_bytes": 227314675, "write_bytes": 67244920}
+KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
+                  "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
 
 def kernel_sources_sha256():
