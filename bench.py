@@ -322,7 +322,7 @@ def main():
                     help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (got --gpus {args.gpus}); "
               f"the DCP shards are simulated on one device", file=sys.stderr)
         sys.exit(2)
     if args.workload == "dense":
