@@ -9,8 +9,10 @@ LSE merge into bf16 out and (T, H) LSE.
 Prints one JSON line on stdout.  `value` is query rows per second of the whole step with
 every input resident in HBM.  `roofline` covers the decode kernel: algorithmic bytes and
 flops per launch over its mean launch time (HIP events on the launch stream).
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same rows.  `cache_write`
-times the fp8_ds_mla cache write of one 32768-token chunk beside the step.
+`unsharded_decode` times the same rows against the unsharded cache (the H = 128 / top-k 2048
+decode, MFMA-bound) after the step.  `cpu_baseline` times the fp64 oracle on a bounded sample
+of the same rows.  `cache_write` times the fp8_ds_mla cache write of one 32768-token chunk
+beside the step.
 """
 from __future__ import annotations
 
@@ -284,7 +286,7 @@ def cpu_baseline(w, budget_s):
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
 DECODE_TRAFFIC = {"sources_sha256": "1535cfdd97bcf6dc747d55b08d2708011554bc2508da84ae54836302aba4c6ac",
-                  "fetch_bytes": 227314675, "write_bytes": 67244920}
+                  "fetch_bytes": 227316455, "write_bytes": 67246384}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
@@ -305,6 +307,12 @@ def measured_traffic():
     return int(t["fetch_bytes"] + t["write_bytes"])
 
 
+def percentiles_us(ms):
+    """p10 / median / p90 of launch durations given in milliseconds, in microseconds."""
+    import numpy as np
+    return [round(float(x) * 1e3, 2) for x in np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,8 +321,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=2, help="cache copies rotated between steps (beat the 256 MB MALL)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--unsharded", action="store_true",
-                    help="also time the unsharded decode of the same rows (reported beside the step)")
+    ap.add_argument("--no-unsharded", action="store_true",
+                    help="skip the unsharded decode of the same rows (timed after the step and reported beside it)")
     ap.add_argument("--workload", choices=("c3", "dense", "bf16"), default="c3",
                     help="c3: the DCP2 MTP step (default); dense: the whole-context MTP decode; bf16: the c3 rows "
                          "unsharded against a plain bf16 cache")
@@ -352,7 +360,7 @@ def main():
     ids = torch.from_numpy(w.ids).to(dev)
     req = torch.from_numpy(w.req).to(dev)
     replicas = [device_shards(w, dev) for _ in range(max(1, args.replicas))]
-    if args.unsharded:
+    if not args.no_unsharded:
         unsharded_cache = w.cache.to_device(dev)
         unsharded_bt = torch.from_numpy(w.block_table).to(dev)
     torch.cuda.synchronize()
@@ -401,12 +409,13 @@ def main():
     roof["traffic"] = measured_traffic()
     roof["kernel"] = "decode_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
     roof["launch_us"] = round(mean_dec_s * 1e6, 2)
+    roof["launch_us_p10_p50_p90"] = percentiles_us(dec_ms)
     roof["algorithmic_bytes"] = int(byts)
     roof["algorithmic_flops"] = int(flops)
     kv_gbps = 656 * sum(shard_valid) * args.steps / (float(np.sum(dec_ms)) / 1e3) / 1e9
 
     unsharded = None
-    if args.unsharded:  # the unsharded H=128 / top-k 2048 decode of the same rows
+    if not args.no_unsharded:  # the unsharded H=128 / top-k 2048 decode of the same rows
         one = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=1, block_size=w.block_size, softmax_scale=w.sm_scale,
                             out_dtype=torch.bfloat16, device=dev)
         for _ in range(3):
@@ -416,9 +425,11 @@ def main():
         for _ in range(max(10, args.steps // 2)):
             one.run(q, ids, req, [(unsharded_cache, unsharded_bt)], decode_events=un_events)
         torch.cuda.synchronize()
-        un_s = float(np.mean([a.elapsed_time(b) for a, b in un_events])) / 1e3
+        un_ms = [a.elapsed_time(b) for a, b in un_events]
+        un_s = float(np.mean(un_ms)) / 1e3
         ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], out_bytes=2)
-        unsharded = {"decode_us": round(un_s * 1e6, 2), "tflops": round(uf / un_s / 1e12, 1),
+        unsharded = {"decode_us": round(un_s * 1e6, 2), "decode_us_p10_p50_p90": percentiles_us(un_ms),
+                     "tflops": round(uf / un_s / 1e12, 1),
                      "kv_gbps": round(656 * nvalid[0] / un_s / 1e9, 1), "roofline": roofline_entry(ub, uf, un_s)}
     cache_write = time_cache_write(dev)
     if args.copy_mib > 0:
