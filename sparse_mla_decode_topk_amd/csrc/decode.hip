@@ -248,11 +248,11 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[hf][r] += sc[hf][r][t] * acc[r];
         }
-      float pv[8];
+      float pv[8];  // raw scores; cq > 0 scales them into log2 units below
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[4 * hf + r] = s[hf][r] * cq;
+        for (int r = 0; r < 4; ++r) pv[4 * hf + r] = s[hf][r];
       if (nin < kTT) {  // tail tile: entries past the end of the list get p = 0
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -261,14 +261,15 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       float mx = pv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, pv[i]);
-      mx = max4x16(mx);
+      mx = max4x16(mx) * cq;  // scaling by cq > 0 commutes with the max
       m_max = fmaxf(m_max, mx);
       m_ref = m_ref == -INFINITY ? mx : m_ref;
       over |= mx > m_ref + kRefHeadroom;
       float lsum = 0.0f;
+      const float nref = -m_ref;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pv[i] = fast_exp2(pv[i] - m_ref);
+        pv[i] = fast_exp2(fmaf(pv[i], cq, nref));
         lsum += pv[i];
       }
       l_run += lsum;

@@ -132,23 +132,24 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
         acc0 = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + 4 * ks * kCS), qv[ks], acc0);
         acc1 = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + 4 * (ks + 1) * kCS), qv[ks + 1], acc1);
       }
-      float pv[4];
+      float pv[4];  // raw scores; cq > 0 scales them into log2 units below
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pv[r] = (acc0[r] + acc1[r]) * cq;
+      for (int r = 0; r < 4; ++r) pv[r] = acc0[r] + acc1[r];
       if (nin < kTT) {  // tail tile: entries past the end of the list get p = 0
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * g + r >= nin) pv[r] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3]));
-      mx = max4x16(mx);
+      mx = max4x16(mx) * cq;  // scaling by cq > 0 commutes with the max
       m_max = fmaxf(m_max, mx);
       m_ref = m_ref == -INFINITY ? mx : m_ref;
       over |= mx > m_ref + kRefHeadroom;
       float lsum = 0.0f;
+      const float nref = -m_ref;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = fast_exp2(pv[r] - m_ref);
+        pv[r] = fast_exp2(fmaf(pv[r], cq, nref));
         lsum += pv[r];
       }
       l_run += lsum;
