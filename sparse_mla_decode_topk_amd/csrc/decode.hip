@@ -215,10 +215,8 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       // ---- S^T for tile n: lane holds head hl, tokens 16hf + 4g + r
       const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
       const int nin = min(kTT, bk.total - n * kTT);
-      int lane_o = lane;
-      asm volatile("" : "+v"(lane_o));  // recompute lane-derived addresses here instead of hoisting them
-      const int tok_a = lane_o & 15;   // record operand row of this lane
-      const int go = lane_o >> 4;
+      const int tok_a = lane & 15;  // record operand row of this lane
+      const int go = lane >> 4;
       f32x4 s[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -339,11 +337,9 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       const int m = n - 1;
       const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
       const uint8_t* pb = sh.pbuf + (m & 1) * kPBuf + vw * kPTile;
-      int lane_o = lane;
-      asm volatile("" : "+v"(lane_o));
-      const int h32 = lane_o & 31, lh = lane_o >> 5;
+      const int h32 = lane & 31, lh = lane >> 5;
       // tr8 row of this lane: record 8(lane/32) + (lane%16)/2, 8-byte half lane&1, chunk (lane/16)&1
-      const int vrow = 16 * (8 * lh + ((lane_o & 15) >> 1)) + 8 * (lane_o & 1) + ((lane_o >> 4) & 1) * kCS;
+      const int vrow = 16 * (8 * lh + ((lane & 15) >> 1)) + 8 * (lane & 1) + ((lane >> 4) & 1) * kCS;
       // all operands of the tile first (tokens past the end carry P' = 0 against real records)
       bf16x8 pf[2][2], va[2][4];
 #pragma unroll

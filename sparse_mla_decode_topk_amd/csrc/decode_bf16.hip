@@ -123,9 +123,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       // ---- S^T for tile n: lane holds head hl, tokens 4g + r
       const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
       const int nin = min(kTT, bk.total - n * kTT);
-      int lane_o = lane;
-      asm volatile("" : "+v"(lane_o));  // recompute lane-derived addresses here instead of hoisting them
-      const uint8_t* kr = tile + 16 * (lane_o & 15) + (lane_o >> 4) * kCS;
+      const uint8_t* kr = tile + 16 * (lane & 15) + (lane >> 4) * kCS;
       f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ks += 2) {
@@ -209,15 +207,13 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       const int m = n - 1;
       const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
       const uint8_t* pb = sh.pbuf + (m & 1) * kPTile;
-      int lane_o = lane;
-      asm volatile("" : "+v"(lane_o));
-      const int h32 = lane_o & 31, lh = lane_o >> 5;
+      const int h32 = lane & 31, lh = lane >> 5;
       bf16x8 pf[2];
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg) pf[hg] = *reinterpret_cast<const bf16x8*>(pb + (32 * hg + h32) * kPRow + 16 * lh);
       // tr16 source of this lane a (in its 16-lane group G = lane / 16): token 8(G/2) + a/4 (+4 for
       // the second read), dims D0 + 4(a%4) .. +3 with D0 = 128vw + 32db + 16(G%2)
-      const int a = lane_o & 15, G = lane_o >> 4;
+      const int a = lane & 15, G = lane >> 4;
       const int dl = 16 * (G & 1) + 4 * (a & 3);  // dim within the 32-dim block, a multiple of 4
       const uint8_t* vsrc = tile + 16 * (8 * (G >> 1) + (a >> 2)) + 2 * (dl & 7) + (dl >> 3) * kCS;
       bf16x8 va[4];
