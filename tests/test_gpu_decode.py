@@ -134,3 +134,38 @@ def test_decode_repeat_is_deterministic():
     a = gpu_decode(w, cache=cache, num_splits=4)
     b = gpu_decode(w, cache=cache, num_splits=4)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _late_dominant(kv):
+    """A row whose head 0 meets, in the 11th 32-entry tile of its list, a record equal to that head's own
+    (unscaled) query: its score then exceeds every score of the first tile by ~200 in log2 units, far past the
+    kernel's fixed-reference headroom of 64, so the workgroup redoes its range with the exact max."""
+    from workload import pack_records, pack_records_bf16
+    w = make_random(321, T=3, H=32, K=400, ctx=600, B=16, n_req=1, kv=kv)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    row, e = 1, 330
+    slot = int(slots[row, e])
+    assert slot >= 0
+    q = w.q_f32()
+    base = q[row, 0].copy()
+    q[row, 0] *= 4.0  # exact in bf16
+    w.q_bits = torch.from_numpy(np.ascontiguousarray(q)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    pack = pack_records if kv == "fp8_ds_mla" else pack_records_bf16
+    i = int(np.searchsorted(w.cache.real_slots, slot))
+    assert w.cache.real_slots[i] == slot
+    w.cache.records[i] = pack(base[None, :512], base[None, 512:])[0]
+    return w, slots
+
+
+@pytest.mark.parametrize("kv", ["fp8_ds_mla", "bf16"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_late_dominant_score_exceeds_headroom(kv, splits):
+    w, slots = _late_dominant(kv)
+    ro, rl = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale, record_layout=kv)
+    # the pinned case: head 0 of row 1 is dominated by the planted record (p ~ 1, a log-sum-exp far above
+    # the first tile's scores)
+    assert rl[1, 0] > 100.0 and np.abs(ro[1, 0]).max() < 8.0
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32,
+                           num_splits=splits, kv_layout=kv)
+    torch.cuda.synchronize()
+    check_close(out, lse, ro, rl, what=f"late dominant {kv} splits {splits}")
