@@ -59,8 +59,8 @@ constexpr int kTileBytes = kChunks * kCS;       // 20992
 constexpr int kStages = 4;                      // tile buffers: scores on n, values on n-1,
 constexpr int kAhead = kStages - 2;             //   loads in flight for n+1 .. n+kAhead
 constexpr int kLoads = (kChunks + 1) / 2;       // 21 global_load_lds per tile, two chunks each
-constexpr int kPRow = 2 * kTT;                  // bytes per head row of a probability tile
-constexpr int kPTile = kHB * kPRow;             // one scale tile of probabilities (4 KB)
+constexpr int kPRow = 2 * kHB;                  // bytes per token row of a probability tile
+constexpr int kPTile = kTT * kPRow;             // one scale tile of probabilities (4 KB)
 constexpr int kPBuf = 4 * kPTile;               // all four scale tiles (16 KB)
 constexpr int kScaleChunk = kScaleOffset / 16;  // 32
 constexpr int kRopeChunk = kRopeOffset / 16;    // 33
@@ -89,6 +89,26 @@ __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+
+// Probability tiles are [token][head] rows of 64 bf16 values (128 bytes) in 8-byte segments of
+// four heads; segment s of token j sits at segment s ^ pswz(j).  pswz swaps the two 2-bit
+// fields of j's low four bits, so both the score waves' stores (sixteen tokens, one segment
+// each) and the value waves' transposed reads (four tokens x four segments per 16-lane
+// group) touch sixteen distinct segments: no bank conflicts either way.
+__device__ __forceinline__ int pswz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
+
+// Max and sum over the 16 lanes of a lane group (lanes 16g .. 16g + 15); every lane of the
+// group gets the same result.
+__device__ __forceinline__ float max16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+  return x;
 }
 
 // Four fp32 values -> packed e4m3 hi terms and the exact residual lo terms.
@@ -199,114 +219,131 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       qr[kk] = w;
     }
   } else {
-    // an idle score wave (fewer than 64 heads) keeps its probability rows at zero
-    for (int i = lane; i < 2 * 4 * 16 * (kPRow / 16); i += 64) {
-      const int seg = i % (kPRow / 16), r = (i / (kPRow / 16)) % 16, tb = i / (16 * (kPRow / 16));
-      *reinterpret_cast<i32x4*>(sh.pbuf + tb * kPTile + (16 * sw + r) * kPRow + 16 * seg) = i32x4{0, 0, 0, 0};
+    // an idle score wave (fewer than 64 heads) keeps its heads' probability segments at zero
+    for (int i = lane; i < 2 * 4 * kTT * 4; i += 64) {
+      const int s = 4 * sw + (i & 3), j = (i >> 2) % kTT, tb = i / (4 * kTT);
+      *reinterpret_cast<i32x2*>(sh.pbuf + tb * kPTile + j * kPRow + 8 * (s ^ pswz(j))) = i32x2{0, 0};
     }
   }
 
-  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.0f;  // per head, same in its four lanes
+  // S = q K^T per 16-token half hf: lane holds token 16hf + tok and heads 16sw + 4g + r (r < 4),
+  // so each lane needs the record scales of only its two tokens.
+  const int tok = lane & 15;
+  float cqo[4];  // cq of the lane's four output heads (lane 4g + r holds head 4g + r's query row)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cqo[r] = __shfl(cq, 4 * g + r);
+  const int pseg = (4 * sw + g) ^ pswz(tok);  // P' segment of this lane's four heads in token row tok
+
+  float m_ref[4], m_raw[4], l_run[4];  // per output head: reference, running raw max, running sum
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m_ref[r] = -INFINITY;
+    m_raw[r] = -INFINITY;
+    l_run[r] = 0.0f;
+  }
   for (int pass = 0; pass < 2; ++pass) {
-    bool over = false;  // a score exceeded the reference by more than the headroom
     for (int n = 0; n <= bk.ntiles; ++n) {
       lds_barrier();  // tile n staged; P'(n-2) consumed by the value waves
       if (!active || n >= bk.ntiles) continue;
-      // ---- S^T for tile n: lane holds head hl, tokens 16hf + 4g + r
       const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
       const int nin = min(kTT, bk.total - n * kTT);
-      const int tok_a = lane & 15;  // record operand row of this lane
-      const int go = lane >> 4;
       f32x4 s[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const uint8_t* kr = tile + 16 * (16 * hf + tok_a);
+        const uint8_t* kr = tile + 16 * (16 * hf + tok);
         f32x4 acc = {};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          acc = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + (kRopeChunk + 4 * kk + go) * kCS), qr[kk], acc);
+          acc = mfma16_bf16(qr[kk], *reinterpret_cast<const bf16x8*>(kr + (kRopeChunk + 4 * kk + g) * kCS), acc);
         s[hf] = acc;
       }
-      f32x4 sc[2][4];  // [hf][r]: the four tile scales of token 16hf + 4g + r
+      f32x4 sc[2];  // [hf]: the four tile scales of token 16hf + tok
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sc[hf][r] = *reinterpret_cast<const f32x4*>(tile + kScaleChunk * kCS + 16 * (16 * hf + 4 * go + r));
+        sc[hf] = *reinterpret_cast<const f32x4*>(tile + kScaleChunk * kCS + 16 * (16 * hf + tok));
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const uint8_t* kr = tile + 16 * (16 * hf + tok_a) + (8 * t + 2 * go) * kCS;
+          const uint8_t* kr = tile + 16 * (16 * hf + tok) + (8 * t + 2 * g) * kCS;
           const i32x4 a0 = *reinterpret_cast<const i32x4*>(kr);
           const i32x4 a1 = *reinterpret_cast<const i32x4*>(kr + kCS);
           const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          f32x4 acc = mfma16_fp8(a, qh[t], f32x4{});
-          acc = mfma16_fp8(a, ql[t], acc);
+          f32x4 acc = mfma16_fp8(qh[t], a, f32x4{});
+          acc = mfma16_fp8(ql[t], a, acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[hf][r] += sc[hf][r][t] * acc[r];
+          for (int r = 0; r < 4; ++r) s[hf][r] += sc[hf][t] * acc[r];
         }
-      float pv[8];  // raw scores; cq > 0 scales them into log2 units below
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[4 * hf + r] = s[hf][r];
       if (nin < kTT) {  // tail tile: entries past the end of the list get p = 0
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (16 * (i >> 2) + 4 * go + (i & 3) >= nin) pv[i] = -INFINITY;
+        for (int hf = 0; hf < 2; ++hf)
+          if (16 * hf + tok >= nin) s[hf] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
-      float mx = pv[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, pv[i]);
-      mx = max4x16(mx) * cq;  // scaling by cq > 0 commutes with the max
-      m_max = fmaxf(m_max, mx);
-      m_ref = m_ref == -INFINITY ? mx : m_ref;
-      over |= mx > m_ref + kRefHeadroom;
-      float lsum = 0.0f;
-      const float nref = -m_ref;
+      for (int r = 0; r < 4; ++r)
+        m_raw[r] = __builtin_elementwise_maximum(m_raw[r], __builtin_elementwise_maximum(s[0][r], s[1][r]));
+      if (pass == 0 && n == 0) {
+        // the reference of the first pass: each head's max over the first tile (scaling by
+        // cq > 0 commutes with the max)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = fast_exp2(fmaf(pv[i], cq, nref));
-        lsum += pv[i];
+        for (int r = 0; r < 4; ++r) m_ref[r] = max16(m_raw[r]) * cqo[r];
       }
-      l_run += lsum;
-      // P'_t = bf16(p * scale(token, t)) as [t][head][token]; 16-byte granule k of a head row
-      // is stored at granule k ^ ((head >> 2) & 3)
-      const int hw = 16 * sw + tok_a;
-      uint8_t* pw = sh.pbuf + (n & 1) * kPBuf + hw * kPRow + 8 * (go & 1);
-      const int swz = (hw >> 2) & 3;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[0][r] = fast_exp2(fmaf(s[0][r], cqo[r], -m_ref[r]));
+        s[1][r] = fast_exp2(fmaf(s[1][r], cqo[r], -m_ref[r]));
+        l_run[r] += s[0][r] + s[1][r];
+      }
+      // P'_t = bf16(p * scale(token, t)) as [t][token][head]
+      uint8_t* pw = sh.pbuf + (n & 1) * kPBuf + tok * kPRow + 8 * pseg;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const bf16x4 v = {(__bf16)(pv[4 * hf] * sc[hf][0][t]), (__bf16)(pv[4 * hf + 1] * sc[hf][1][t]),
-                            (__bf16)(pv[4 * hf + 2] * sc[hf][2][t]), (__bf16)(pv[4 * hf + 3] * sc[hf][3][t])};
-          *reinterpret_cast<bf16x4*>(pw + t * kPTile + 16 * ((2 * hf + (go >> 1)) ^ swz)) = v;
+          const float f = sc[hf][t];
+          const bf16x4 v = {(__bf16)(s[hf][0] * f), (__bf16)(s[hf][1] * f), (__bf16)(s[hf][2] * f),
+                            (__bf16)(s[hf][3] * f)};
+          *reinterpret_cast<bf16x4*>(pw + t * kPTile + 16 * hf * kPRow) = v;
         }
     }
     // a second pass, with the exact max as reference, only if some score outgrew the headroom
+    bool over = false;
+    float m_max[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_max[r] = active ? max16(m_raw[r]) * cqo[r] : -INFINITY;
+      over |= m_max[r] > m_ref[r] + kRefHeadroom;
+    }
     if (!__syncthreads_or(over)) break;
-    m_ref = m_max;
-    l_run = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_ref[r] = m_max[r];
+      m_raw[r] = -INFINITY;
+      l_run[r] = 0.0f;
+    }
   }
 
   // ---- per-head (max, sum) for the value waves; lse or the split partial
   if (active) {
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const float mo = l_tot > 0.0f ? m_ref : -INFINITY;
-    if (g == 0) {
-      sh.ml[2 * hl] = mo;
-      sh.ml[2 * hl + 1] = l_tot;
-      const int head = bk.h_lo + hl;
-      if (p.splits == 1) {
-        p.lse[(int64_t)bk.row * p.l_st + (int64_t)head * p.l_sh] =
-            l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-      } else {
-        const int64_t pidx = ((int64_t)bk.row * p.splits + bk.split) * p.H + head;
-        p.ws_ml[pidx * 2 + 0] = mo;
-        p.ws_ml[pidx * 2 + 1] = l_tot;
+    float l_tot[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_tot[r] = sum16(l_run[r]);
+    if (tok == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * sw + 4 * g + r;
+        const float mo = l_tot[r] > 0.0f ? m_ref[r] : -INFINITY;
+        sh.ml[2 * h] = mo;
+        sh.ml[2 * h + 1] = l_tot[r];
+        const int head = bk.h_lo + h;
+        if (p.splits == 1) {
+          p.lse[(int64_t)bk.row * p.l_st + (int64_t)head * p.l_sh] =
+              l_tot[r] > 0.0f ? (m_ref[r] + __log2f(l_tot[r])) * kLn2 : -INFINITY;
+        } else {
+          const int64_t pidx = ((int64_t)bk.row * p.splits + bk.split) * p.H + head;
+          p.ws_ml[pidx * 2 + 0] = mo;
+          p.ws_ml[pidx * 2 + 1] = l_tot[r];
+        }
       }
     }
   }
@@ -319,6 +356,22 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, const Block& bk, int vw, int lane) {
   // O^T blocks o[db][hg]: dims 128vw + 32db + 8(r/4) + 4(lane/32) + r%4, head 32hg + lane%32
   f32x16 o[4][2];
+  // P'^T operand of head block hg (heads 32hg + lane%32, tokens 16ks + 8(lane/32) .. +7) as two
+  // transposed reads: in its 16-lane group G the lane a addresses token T0 + a/4 (T0 = 16ks +
+  // 8(G/2), then + 4) and heads H0 + 4(a%4) .. +3 (H0 = 32hg + 16(G%2)), and receives head H0 + a
+  // of the four tokens.  Offsets within a probability tile, less the 16ks token rows.
+  int poff[2][2];
+  {
+    const int G = lane >> 4, a = lane & 15;
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int tk = 8 * (G >> 1) + (a >> 2) + 4 * half;
+        const int seg = 8 * hg + 4 * (G & 1) + (a & 3);
+        poff[hg][half] = tk * kPRow + 8 * (seg ^ pswz(tk));
+      }
+  }
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -337,7 +390,7 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       const int m = n - 1;
       const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
       const uint8_t* pb = sh.pbuf + (m & 1) * kPBuf + vw * kPTile;
-      const int h32 = lane & 31, lh = lane >> 5;
+      const int lh = lane >> 5;
       // tr8 row of this lane: record 8(lane/32) + (lane%16)/2, 8-byte half lane&1, chunk (lane/16)&1
       const int vrow = 16 * (8 * lh + ((lane & 15) >> 1)) + 8 * (lane & 1) + ((lane >> 4) & 1) * kCS;
       // all operands of the tile first (tokens past the end carry P' = 0 against real records)
@@ -346,8 +399,10 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       for (int ks = 0; ks < kTT / 16; ++ks) {
 #pragma unroll
         for (int hg = 0; hg < 2; ++hg) {
-          const int hl = 32 * hg + h32;
-          pf[ks][hg] = *reinterpret_cast<const bf16x8*>(pb + hl * kPRow + 16 * ((2 * ks + lh) ^ ((hl >> 2) & 3)));
+          const uint8_t* src = pb + ks * 16 * kPRow;
+          const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS i16x4*)(src + poff[hg][0]));
+          const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS i16x4*)(src + poff[hg][1]));
+          pf[ks][hg] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {

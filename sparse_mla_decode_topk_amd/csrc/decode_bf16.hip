@@ -31,7 +31,6 @@ namespace {
 
 using namespace dec;
 
-typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 constexpr int kRecB = 2 * kHeadDim;          // 1152 bytes per record
 constexpr int kTT = 16;                      // records per tile

@@ -21,6 +21,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 #define SMLA_LDS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.69314718055994530942f;
