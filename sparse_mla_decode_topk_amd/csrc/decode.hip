@@ -87,8 +87,9 @@ __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+// A x B on fp8 with the A rows scaled by 2^(sa - 127) (E8M0 sa, this lane's row) and unit B scales.
+__device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, kUnitScale);
 }
 
 // Probability tiles are [token][head] rows of 64 bf16 values (128 bytes) in 8-byte segments of
@@ -166,8 +167,8 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
   const int hl = 16 * sw + (lane & 15);  // head within the block
   const bool active = 16 * sw < bk.nh;
   i32x8 qh[4], ql[4];  // q * 2^e as e4m3 hi / lo: byte i of tile t <-> dim 128t + 32g + i
-  bf16x8 qr[2];        // rope q * 2^e: element i of kk <-> rope dim 32kk + 8g + i
-  float cq = 0.0f;     // softmax_scale * log2(e) * 2^-e
+  bf16x8 qr[2];        // rope q (bf16 as given): element i of kk <-> rope dim 32kk + 8g + i
+  int qsa = kUnitScale;  // E8M0 of 2^-e: the latent MFMAs scale q's rows back by it
   if (active) {
     const uint16_t* qp = p.q + (int64_t)bk.row * p.q_st + (int64_t)(bk.h_lo + hl) * p.q_sh;
     // pass 1: per-head max |q| (lanes l, l^16, l^32, l^48 hold one head)
@@ -194,7 +195,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       if (ldexpf(amax, e) > 448.0f) --e;
       e = max(-100, min(100, e));
     }
-    cq = p.scale_log2 * ldexpf(1.0f, -e);
+    qsa = kUnitScale - e;
     // pass 2: q * 2^e = hi + lo, both e4m3
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -212,11 +213,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * kk + 8 * g);
-      bf16x8 w;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = (__bf16)ldexpf((float)v[i], e);  // exact: |q * 2^e| <= 448
-      qr[kk] = w;
+      qr[kk] = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * kk + 8 * g);
     }
   } else {
     // an idle score wave (fewer than 64 heads) keeps its heads' probability segments at zero
@@ -229,9 +226,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
   // S = q K^T per 16-token half hf: lane holds token 16hf + tok and heads 16sw + 4g + r (r < 4),
   // so each lane needs the record scales of only its two tokens.
   const int tok = lane & 15;
-  float cqo[4];  // cq of the lane's four output heads (lane 4g + r holds head 4g + r's query row)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) cqo[r] = __shfl(cq, 4 * g + r);
+  const float cq = p.scale_log2;  // scores come out in true units: softmax_scale * log2(e)
   const int pseg = (4 * sw + g) ^ pswz(tok);  // P' segment of this lane's four heads in token row tok
 
   float m_ref[4], m_raw[4], l_run[4];  // per output head: reference, running raw max, running sum
@@ -269,8 +264,8 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
           const i32x4 a0 = *reinterpret_cast<const i32x4*>(kr);
           const i32x4 a1 = *reinterpret_cast<const i32x4*>(kr + kCS);
           const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          f32x4 acc = mfma16_fp8(qh[t], a, f32x4{});
-          acc = mfma16_fp8(ql[t], a, acc);
+          f32x4 acc = mfma16_fp8(qh[t], a, f32x4{}, qsa);
+          acc = mfma16_fp8(ql[t], a, acc, qsa);
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[hf][r] += sc[hf][t] * acc[r];
         }
@@ -286,12 +281,12 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
         // the reference of the first pass: each head's max over the first tile (scaling by
         // cq > 0 commutes with the max)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m_ref[r] = max16(m_raw[r]) * cqo[r];
+        for (int r = 0; r < 4; ++r) m_ref[r] = max16(m_raw[r]) * cq;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[0][r] = fast_exp2(fmaf(s[0][r], cqo[r], -m_ref[r]));
-        s[1][r] = fast_exp2(fmaf(s[1][r], cqo[r], -m_ref[r]));
+        s[0][r] = fast_exp2(fmaf(s[0][r], cq, -m_ref[r]));
+        s[1][r] = fast_exp2(fmaf(s[1][r], cq, -m_ref[r]));
         l_run[r] += s[0][r] + s[1][r];
       }
       // P'_t = bf16(p * scale(token, t)) as [t][token][head]
@@ -311,7 +306,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
     float m_max[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m_max[r] = active ? max16(m_raw[r]) * cqo[r] : -INFINITY;
+      m_max[r] = active ? max16(m_raw[r]) * cq : -INFINITY;
       over |= m_max[r] > m_ref[r] + kRefHeadroom;
     }
     if (!__syncthreads_or(over)) break;

@@ -91,19 +91,19 @@ __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
 
 // Compacts this split's slot entries that lie in [0, num_slots) into sh.clist, in order;
 // returns their number.  No front-pack is needed upstream.
-template <class SH>
+template <class SH, int NT = kThreads>
 __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block& bk, SH& sh, int tid, int wave,
                                              int lane) {
   const int e0 = bk.split * p.entries_per_split;
   const int e1 = min(p.K, e0 + p.entries_per_split);
   const int32_t* srow = p.slots + (int64_t)bk.row * p.slots_ld;
   int total = 0;
-  for (int base = e0; base < e1; base += kThreads * 4) {
+  for (int base = e0; base < e1; base += NT * 4) {
     int vals[4];
     int wcount = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = base + i * kThreads + tid;
+      const int e = base + i * NT + tid;
       const int v = e < e1 ? srow[e] : -1;
       const bool ok = v >= 0 && (int64_t)v < p.num_slots;
       vals[i] = ok ? v : -1;
@@ -113,7 +113,7 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
     __syncthreads();
     int off = total, all = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
       const int c = sh.wave_cnt[w];
       off += w < wave ? c : 0;
       all += c;
@@ -137,7 +137,7 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
 // head's LSE); then each thread owns 4 dims of every fourth head and, split by split, loads
 // all of its partial rows before accumulating them, so the merge costs one memory round trip
 // per split rather than several per output element.
-template <class SH>
+template <class SH, int NT = kThreads>
 __device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, SH& sh, int tid) {
   float* wts = reinterpret_cast<float*>(sh.stage);  // [head][split]; the tile buffers are free now
   if (tid < bk.nh) {
@@ -162,7 +162,7 @@ __device__ __forceinline__ void combine_splits(const DecodeParams& p, const Bloc
     p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
   }
   __syncthreads();
-  constexpr int kPerThread = kHB * (kLatent / 4) / kThreads;  // 16 (head, 4-dim) items per thread
+  constexpr int kPerThread = kHB * (kLatent / 4) / NT;  // (head, 4-dim) items per thread
   const int d4 = tid % (kLatent / 4);
   const int h0 = tid / (kLatent / 4);  // heads h0, h0 + 4, ... (wave-uniform)
   f32x4 acc[kPerThread];
@@ -172,7 +172,7 @@ __device__ __forceinline__ void combine_splits(const DecodeParams& p, const Bloc
     f32x4 part[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int hl = h0 + (kThreads / (kLatent / 4)) * i;
+      const int hl = h0 + (NT / (kLatent / 4)) * i;
       part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (hl < bk.nh && wts[hl * p.splits + sp] != 0.0f) {
         const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + bk.h_lo + hl;
@@ -181,13 +181,13 @@ __device__ __forceinline__ void combine_splits(const DecodeParams& p, const Bloc
     }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int hl = h0 + (kThreads / (kLatent / 4)) * i;
+      const int hl = h0 + (NT / (kLatent / 4)) * i;
       if (hl < bk.nh) acc[i] += wts[hl * p.splits + sp] * part[i];
     }
   }
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int hl = h0 + (kThreads / (kLatent / 4)) * i;
+    const int hl = h0 + (NT / (kLatent / 4)) * i;
     if (hl >= bk.nh) continue;
     const int h = bk.h_lo + hl;
     if (p.out_fp32) {
