@@ -18,14 +18,16 @@
 //    with global_load_lds_dwordx4 by the value waves, kAhead tiles ahead.  One load moves
 //    two 16-byte chunks of all 32 records, so a tile sits chunk-major in LDS
 //    ([41 chunks][32 records][16 B]) and every MFMA operand read is contiguous.
-//  * QK^T latent part on v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales): the raw e4m3
-//    codes are the record operand as stored; q is split exactly into two e4m3 terms,
-//    q * 2^e_h = hi + lo (hi = rne(q * 2^e_h), lo = rne(q * 2^e_h - hi), e_h a per-head power
-//    of two that puts max|q| just under 448; exact wherever |q * 2^e_h| >= 2^-2), so two fp8
-//    MFMAs give the bf16-exact product at the cost of one bf16 MFMA and no widening.  One
-//    MFMA k-step spans exactly one 128-dim scale tile, whose fp32 record scale then
-//    multiplies that tile's partial dot product.  Rope dims (bf16) run on
-//    v_mfma_f32_16x16x32_bf16.  Scores come out as S^T (tokens x heads): one head per lane.
+//  * QK^T latent part on v_mfma_scale_f32_16x16x128_f8f6f4: the raw e4m3 codes are the
+//    record operand as stored; q is split exactly into two e4m3 terms, q * 2^e_h = hi + lo
+//    (hi = rne(q * 2^e_h), lo = rne(q * 2^e_h - hi), e_h a per-head power of two that puts
+//    max|q| just under 448; exact wherever |q * 2^e_h| >= 2^-2), so two fp8 MFMAs give the
+//    bf16-exact product at the cost of one bf16 MFMA and no widening; the MFMA's E8M0 scale
+//    of each q row takes 2^-e_h back out.  One MFMA k-step spans exactly one 128-dim scale
+//    tile, whose fp32 record scale then multiplies that tile's partial dot product.  Rope
+//    dims (bf16) run on v_mfma_f32_16x16x32_bf16.  Scores come out as heads x tokens: a lane
+//    holds one token of each 16-token half and four heads, so it needs the record scales of
+//    two tokens only, and keeps a running max per head without cross-lane work per tile.
 //  * Softmax in base 2 against a per-head reference max fixed at the first tile: later
 //    probabilities are 2^(s - ref) and may exceed 1, which fp32 accumulators and bf16
 //    probabilities hold without loss.  Should a score ever exceed the reference by more
@@ -34,8 +36,9 @@
 //    wait on a max.
 //  * PV: O^T[dim, head] += V^T[dim, token] . P'^T[token, head] on bf16 MFMA, with
 //    P' = p * scale(token, tile) rounded once to bf16 and handed over in LDS per scale tile
-//    (double-buffered); V^T fragments come straight from the staged tile through
-//    ds_read_b64_tr_b8 and are widened exactly.
+//    as [token][head] rows (double-buffered), read back transposed by ds_read_b64_tr_b16;
+//    V^T fragments come straight from the staged tile through ds_read_b64_tr_b8 and are
+//    widened exactly.
 //  * One workgroup barrier per tile orders it all: tile n staged, P'(n-1) written, and
 //    tile n-2 plus P'(n-2) consumed, so its buffers may be refilled.
 //  * Split-K over the top-k list with an in-kernel combine: every split writes its
