@@ -48,6 +48,8 @@
 
 #include "decode_common.h"
 
+#include <stddef.h>
+
 namespace smla {
 namespace {
 
@@ -73,14 +75,31 @@ static_assert(kAhead >= 1 && kAhead <= 3, "load waits below cover up to 3 tiles 
 static_assert(kHB * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile buffers");
 static_assert(kHB * (kLatent / 4) % kThreads == 0 && kThreads % (kLatent / 4) == 0, "combine item split");
 
+// Output staging rows after the tile loop: 16 bytes of padding put consecutive rows four
+// banks apart, so the value waves' row-strided writes do not conflict.
+constexpr int kOutPitch32 = 4 * kLatent + 16;  // fp32 rows
+constexpr int kOutPitch16 = 2 * kLatent + 16;  // bf16 rows
+
 struct Shared {
-  uint8_t stage[kStages * kTileBytes];
-  uint8_t pbuf[2 * kPBuf];
+  uint8_t stage[kStages * kTileBytes];  // followed directly by pbuf and clist: the output staging
+  uint8_t pbuf[2 * kPBuf];              // rows span all three once the tile loop is done
   int32_t clist[kMaxEntriesPerSplit];
   float ml[2 * kHB];  // per head of the block: (reference max, sum)
   int32_t wave_cnt[kThreads / 64];
   int32_t last_flag;
 };
+static_assert(offsetof(Shared, pbuf) == offsetof(Shared, stage) + sizeof(Shared::stage) &&
+                  offsetof(Shared, clist) == offsetof(Shared, pbuf) + sizeof(Shared::pbuf),
+              "tile, probability and slot-list buffers are contiguous");
+static_assert(kStages * kTileBytes + 2 * kPBuf + 4 * kMaxEntriesPerSplit >= kHB * kOutPitch32,
+              "output staging rows fit in the tile, probability and slot-list buffers");
+static_assert(kHB * (4 * kLatent / 16) % kThreads == 0 && kHB * (2 * kLatent / 16) % kThreads == 0, "row store split");
+
+// Start of the output staging rows (the tile, probability and slot-list buffers as one span).
+__device__ __forceinline__ uint8_t* staging(Shared& sh) { return reinterpret_cast<uint8_t*>(&sh) + offsetof(Shared, stage); }
+__device__ __forceinline__ const uint8_t* staging(const Shared& sh) {
+  return reinterpret_cast<const uint8_t*>(&sh) + offsetof(Shared, stage);
+}
 
 __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -174,22 +193,21 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
   int qsa = kUnitScale;  // E8M0 of 2^-e: the latent MFMAs scale q's rows back by it
   if (active) {
     const uint16_t* qp = p.q + (int64_t)bk.row * p.q_st + (int64_t)(bk.h_lo + hl) * p.q_sh;
-    // pass 1: per-head max |q| (lanes l, l^16, l^32, l^48 hold one head)
-    float amax = 0.0f;
+    // pass 1: per-head max |q| over the latent dims (the rope dims are used as given), as an
+    // integer max of the bf16 magnitude bits, two values per instruction (lanes l, l^16, l^32,
+    // l^48 hold one head)
+    typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+    u16x2 mbits = {0, 0};
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 128 * t + 32 * g + 8 * c);
+        const i32x4 v = *reinterpret_cast<const i32x4*>(qp + 128 * t + 32 * g + 8 * c);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
+        for (int i = 0; i < 4; ++i)
+          mbits = __builtin_elementwise_max(mbits, __builtin_bit_cast(u16x2, (uint32_t)v[i] & 0x7FFF7FFFu));
       }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * kk + 8 * g);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)v[i]));
-    }
+    float amax = __uint_as_float((uint32_t)max(mbits[0], mbits[1]) << 16);
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     int e = 0;
@@ -421,43 +439,76 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
   }
   __syncthreads();  // the score waves' (max, sum) are in LDS
 
+  // ---- O (normalised when this is the only split) into LDS rows [head][dim], fp32 or bf16, in
+  // the tile, probability and slot-list buffers, which are free now; all eight waves then
+  // store whole rows (store_rows)
+  const bool f32out = p.splits > 1 || p.out_fp32;
   const int h32 = lane & 31;
   const int dbase = 128 * vw + 4 * (lane >> 5);  // + 32db + 8qd
 #pragma unroll
   for (int hg = 0; hg < 2; ++hg) {
     const int hl = 32 * hg + h32;
-    if (hl >= bk.nh) continue;
-    const int head = bk.h_lo + hl;
+    float inv = 1.0f;
     if (p.splits == 1) {
       const float lt = sh.ml[2 * hl + 1];
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      if (p.out_fp32) {
-        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd) =
-                f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
-      } else {
-        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * qd) =
-                bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
-                       (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
-      }
-    } else {
-      // split-K: this split's unnormalised partial
-      float* po = p.ws_o + (((int64_t)bk.row * p.splits + bk.split) * p.H + head) * kLatent + dbase;
+      inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    }
+    if (f32out) {
+      float* r = reinterpret_cast<float*>(staging(sh) + hl * kOutPitch32) + dbase;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd) =
-              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]};
+          *reinterpret_cast<f32x4*>(r + 32 * db + 8 * qd) =
+              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
+    } else {
+      __bf16* r = reinterpret_cast<__bf16*>(staging(sh) + hl * kOutPitch16) + dbase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<bf16x4*>(r + 32 * db + 8 * qd) =
+              bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
+                     (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
+    }
+  }
+}
+
+// Staged output rows -> global memory, 16 bytes per thread and 1 KB of one row per wave and
+// instruction (a direct store from the MFMA layout would touch 32 rows per instruction).
+// Rows of heads past the block's last head are not written.
+__device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& bk, const Shared& sh, int tid) {
+  if (p.splits > 1 || p.out_fp32) {
+    float* base;
+    int64_t hstride;
+    if (p.splits > 1) {  // this split's unnormalised partial
+      base = p.ws_o + ((int64_t)bk.row * p.splits + bk.split) * p.H * kLatent;
+      hstride = kLatent;
+    } else {
+      base = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st;
+      hstride = p.o_sh;
+    }
+    constexpr int kChunksPerRow = 4 * kLatent / 16;  // 128
+#pragma unroll
+    for (int k = 0; k < kHB * kChunksPerRow / kThreads; ++k) {
+      const int c = tid + kThreads * k;
+      const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
+      if (hl < bk.nh) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(staging(sh) + hl * kOutPitch32 + 16 * col);
+        *reinterpret_cast<f32x4*>(base + (int64_t)(bk.h_lo + hl) * hstride + 4 * col) = v;
+      }
+    }
+  } else {
+    __bf16* base = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st;
+    constexpr int kChunksPerRow = 2 * kLatent / 16;  // 64
+#pragma unroll
+    for (int k = 0; k < kHB * kChunksPerRow / kThreads; ++k) {
+      const int c = tid + kThreads * k;
+      const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
+      if (hl < bk.nh) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(staging(sh) + hl * kOutPitch16 + 16 * col);
+        *reinterpret_cast<i32x4*>(base + (int64_t)(bk.h_lo + hl) * p.o_sh + 8 * col) = v;
+      }
     }
   }
 }
@@ -478,6 +529,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     score_role(p, sh, bk, wave, lane);
   else
     value_role(p, sh, bk, wave - 4, lane);
+  __syncthreads();  // output rows staged
+  store_rows(p, bk, sh, tid);
   if (p.splits == 1) return;
 
   if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, tid);
