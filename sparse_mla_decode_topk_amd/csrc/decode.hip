@@ -48,8 +48,6 @@
 
 #include "decode_common.h"
 
-#include <stddef.h>
-
 namespace smla {
 namespace {
 
@@ -75,11 +73,6 @@ static_assert(kAhead >= 1 && kAhead <= 3, "load waits below cover up to 3 tiles 
 static_assert(kHB * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile buffers");
 static_assert(kHB * (kLatent / 4) % kThreads == 0 && kThreads % (kLatent / 4) == 0, "combine item split");
 
-// Output staging rows after the tile loop: 16 bytes of padding put consecutive rows four
-// banks apart, so the value waves' row-strided writes do not conflict.
-constexpr int kOutPitch32 = 4 * kLatent + 16;  // fp32 rows
-constexpr int kOutPitch16 = 2 * kLatent + 16;  // bf16 rows
-
 struct Shared {
   uint8_t stage[kStages * kTileBytes];  // followed directly by pbuf and clist: the output staging
   uint8_t pbuf[2 * kPBuf];              // rows span all three once the tile loop is done
@@ -91,7 +84,7 @@ struct Shared {
 static_assert(offsetof(Shared, pbuf) == offsetof(Shared, stage) + sizeof(Shared::stage) &&
                   offsetof(Shared, clist) == offsetof(Shared, pbuf) + sizeof(Shared::pbuf),
               "tile, probability and slot-list buffers are contiguous");
-static_assert(kStages * kTileBytes + 2 * kPBuf + 4 * kMaxEntriesPerSplit >= kHB * kOutPitch32,
+static_assert(kStages * kTileBytes + 2 * kPBuf + 4 * kMaxEntriesPerSplit >= kOutStageBytes,
               "output staging rows fit in the tile, probability and slot-list buffers");
 static_assert(kHB * (4 * kLatent / 16) % kThreads == 0 && kHB * (2 * kLatent / 16) % kThreads == 0, "row store split");
 
@@ -112,26 +105,6 @@ __device__ __forceinline__ bf16x8 widen_fp8x8(uint32_t lo, uint32_t hi) {
 // A x B on fp8 with the A rows scaled by 2^(sa - 127) (E8M0 sa, this lane's row) and unit B scales.
 __device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c, int sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, kUnitScale);
-}
-
-// Probability tiles are [token][head] rows of 64 bf16 values (128 bytes) in 8-byte segments of
-// four heads; segment s of token j sits at segment s ^ pswz(j).  pswz swaps the two 2-bit
-// fields of j's low four bits, so both the score waves' stores (sixteen tokens, one segment
-// each) and the value waves' transposed reads (four tokens x four segments per 16-lane
-// group) touch sixteen distinct segments: no bank conflicts either way.
-__device__ __forceinline__ int pswz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
-
-// Max and sum over the 16 lanes of a lane group (lanes 16g .. 16g + 15); every lane of the
-// group gets the same result.
-__device__ __forceinline__ float max16(float x) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
-  return x;
 }
 
 // Four fp32 values -> packed e4m3 hi terms and the exact residual lo terms.
@@ -438,79 +411,7 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
     if (!__syncthreads_or(false)) break;
   }
   __syncthreads();  // the score waves' (max, sum) are in LDS
-
-  // ---- O (normalised when this is the only split) into LDS rows [head][dim], fp32 or bf16, in
-  // the tile, probability and slot-list buffers, which are free now; all eight waves then
-  // store whole rows (store_rows)
-  const bool f32out = p.splits > 1 || p.out_fp32;
-  const int h32 = lane & 31;
-  const int dbase = 128 * vw + 4 * (lane >> 5);  // + 32db + 8qd
-#pragma unroll
-  for (int hg = 0; hg < 2; ++hg) {
-    const int hl = 32 * hg + h32;
-    float inv = 1.0f;
-    if (p.splits == 1) {
-      const float lt = sh.ml[2 * hl + 1];
-      inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    }
-    if (f32out) {
-      float* r = reinterpret_cast<float*>(staging(sh) + hl * kOutPitch32) + dbase;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<f32x4*>(r + 32 * db + 8 * qd) =
-              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
-    } else {
-      __bf16* r = reinterpret_cast<__bf16*>(staging(sh) + hl * kOutPitch16) + dbase;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<bf16x4*>(r + 32 * db + 8 * qd) =
-              bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
-                     (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
-    }
-  }
-}
-
-// Staged output rows -> global memory, 16 bytes per thread and 1 KB of one row per wave and
-// instruction (a direct store from the MFMA layout would touch 32 rows per instruction).
-// Rows of heads past the block's last head are not written.
-__device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& bk, const Shared& sh, int tid) {
-  if (p.splits > 1 || p.out_fp32) {
-    float* base;
-    int64_t hstride;
-    if (p.splits > 1) {  // this split's unnormalised partial
-      base = p.ws_o + ((int64_t)bk.row * p.splits + bk.split) * p.H * kLatent;
-      hstride = kLatent;
-    } else {
-      base = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st;
-      hstride = p.o_sh;
-    }
-    constexpr int kChunksPerRow = 4 * kLatent / 16;  // 128
-#pragma unroll
-    for (int k = 0; k < kHB * kChunksPerRow / kThreads; ++k) {
-      const int c = tid + kThreads * k;
-      const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
-      if (hl < bk.nh) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(staging(sh) + hl * kOutPitch32 + 16 * col);
-        *reinterpret_cast<f32x4*>(base + (int64_t)(bk.h_lo + hl) * hstride + 4 * col) = v;
-      }
-    }
-  } else {
-    __bf16* base = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st;
-    constexpr int kChunksPerRow = 2 * kLatent / 16;  // 64
-#pragma unroll
-    for (int k = 0; k < kHB * kChunksPerRow / kThreads; ++k) {
-      const int c = tid + kThreads * k;
-      const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
-      if (hl < bk.nh) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(staging(sh) + hl * kOutPitch16 + 16 * col);
-        *reinterpret_cast<i32x4*>(base + (int64_t)(bk.h_lo + hl) * p.o_sh + 8 * col) = v;
-      }
-    }
-  }
+  stage_output(p, sh.ml, staging(sh), o, vw, lane);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
@@ -530,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
   else
     value_role(p, sh, bk, wave - 4, lane);
   __syncthreads();  // output rows staged
-  store_rows(p, bk, sh, tid);
+  store_rows(p, bk, staging(sh), tid);
   if (p.splits == 1) return;
 
   if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, tid);

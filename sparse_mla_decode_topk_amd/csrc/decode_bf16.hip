@@ -14,11 +14,13 @@
 //    so a tile sits chunk-major in LDS ([72 chunks][16 records][16 B]).
 //  * QK^T on v_mfma_f32_16x16x32_bf16 over all 576 dims (18 k-steps, two accumulators):
 //    the record's bf16 values are the operand as stored, q stays in registers as bf16, and
-//    scores come out as S^T (tokens x heads), one head per lane.  No per-tile scale.
+//    scores come out as heads x tokens (a lane holds one token and four heads), so the max
+//    runs per lane with no cross-lane work per tile.  No per-tile scale.
 //  * Softmax in base 2 against a per-head reference max fixed at the first tile (a second
 //    pass with the exact max if a score ever exceeds it by more than 2^64), so the output
-//    accumulators are never rescaled; P = bf16(p) goes to LDS once per tile as
-//    [head][token] rows padded to 48 bytes (conflict-free reads).
+//    accumulators are never rescaled; P = bf16(p) goes to LDS once per tile as swizzled
+//    [token][head] rows that the value waves read back transposed (ds_read_b64_tr_b16).
+//  * The output leaves through LDS-staged rows, whole rows per store instruction.
 //  * PV on v_mfma_f32_32x32x16_bf16: O^T[dim, head] += V^T[dim, token] . P^T[token, head];
 //    the V^T operand comes straight from the staged tile through two ds_read_b64_tr_b16 per
 //    32-dim block (lane i of a 16-lane group receives dim D0 + i of four consecutive tokens).
@@ -41,21 +43,32 @@ constexpr int kStages = 6;                   // tile buffers: scores on n, value
 constexpr int kAhead = kStages - 2;          //   loads in flight for n+1 .. n+kAhead
 constexpr int kLoads = kChunks / 4;          // 18 global_load_lds per tile, four chunks each
 constexpr int kKSteps = kHeadDim / 32;       // 18 QK k-steps of 32 dims
-constexpr int kPRow = 48;                    // bytes per head row of a probability tile (32 used)
-constexpr int kPTile = kHB * kPRow;          // 3 KB
+constexpr int kPRow = 2 * kHB;               // bytes per token row of a probability tile
+constexpr int kPTile = kTT * kPRow;          // 2 KB
+// the probability buffers, sized so that the tile, probability and slot-list buffers together
+// hold the output staging rows after the loop
+constexpr int kPSpan = 2 * kPTile > kOutStageBytes - kStages * kTileBytes - 4 * kMaxEntriesPerSplit
+                           ? 2 * kPTile
+                           : kOutStageBytes - kStages * kTileBytes - 4 * kMaxEntriesPerSplit;
 
 static_assert(kRecB % 64 == 0, "a copy moves four whole chunks");
 static_assert(kAhead == 4, "load waits below are written for 4 tiles ahead");
 static_assert(kHB * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile buffers");
 
 struct Shared {
-  uint8_t stage[kStages * kTileBytes];
-  uint8_t pbuf[2 * kPTile];
+  uint8_t stage[kStages * kTileBytes];  // followed directly by pbuf and clist: the output staging
+  uint8_t pbuf[kPSpan];                 // rows span all three once the tile loop is done
   int32_t clist[kMaxEntriesPerSplit];
   float ml[2 * kHB];  // per head of the block: (reference max, sum)
   int32_t wave_cnt[kThreads / 64];
   int32_t last_flag;
 };
+static_assert(offsetof(Shared, pbuf) == offsetof(Shared, stage) + sizeof(Shared::stage) &&
+                  offsetof(Shared, clist) == offsetof(Shared, pbuf) + sizeof(Shared::pbuf) &&
+                  sizeof(Shared::stage) + sizeof(Shared::pbuf) + sizeof(Shared::clist) >= kOutStageBytes,
+              "tile, probability and slot-list buffers are contiguous and hold the output staging rows");
+
+__device__ __forceinline__ uint8_t* staging(Shared& sh) { return reinterpret_cast<uint8_t*>(&sh) + offsetof(Shared, stage); }
 
 // Copies value wave b issues per tile: copy j of a tile belongs to wave j % 4.
 __device__ __forceinline__ int loads_of_wave(int b) { return b < kLoads % 4 ? kLoads / 4 + 1 : kLoads / 4; }
@@ -93,11 +106,12 @@ __device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, con
 }
 
 // ---------------------------------------------------------------------------------------
-// Score wave `sw` (0..3): heads h_lo + 16sw + (lane & 15); lane group g = lane >> 4 holds
-// the query dims 32ks + 8g .. +7 of every k-step ks.
+// Score wave `sw` (0..3): heads h_lo + 16sw + 0..15.  Query operand: lane holds head
+// 16sw + (lane & 15) and dims 32ks + 8g .. +7 of every k-step ks (g = lane >> 4).  Scores
+// S = q K^T come out as heads x tokens: lane holds token (lane & 15) and heads 16sw + 4g + r.
 __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, const Block& bk, int sw, int lane) {
   const int g = lane >> 4;
-  const int hl = 16 * sw + (lane & 15);  // head within the block
+  const int hl = 16 * sw + (lane & 15);  // head of this lane's query operand row
   const bool active = 16 * sw < bk.nh;
   bf16x8 qv[kKSteps];
   if (active) {
@@ -105,77 +119,97 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qv[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * g);
   } else {
-    // an idle score wave (fewer than 64 heads) keeps its probability rows at zero
-    for (int i = lane; i < 2 * 16 * (kPRow / 16); i += 64) {
-      const int seg = i % (kPRow / 16), r = (i / (kPRow / 16)) % 16, tb = i / (16 * (kPRow / 16));
-      *reinterpret_cast<i32x4*>(sh.pbuf + tb * kPTile + (16 * sw + r) * kPRow + 16 * seg) = i32x4{0, 0, 0, 0};
+    // an idle score wave (fewer than 64 heads) keeps its heads' probability segments at zero
+    for (int i = lane; i < 2 * kTT * 4; i += 64) {
+      const int s4 = 4 * sw + (i & 3), j = (i >> 2) % kTT, b = i / (4 * kTT);
+      *reinterpret_cast<i32x2*>(sh.pbuf + b * kPTile + j * kPRow + 8 * (s4 ^ pswz(j))) = i32x2{0, 0};
     }
   }
   const float cq = p.scale_log2;
+  const int tok = lane & 15;
+  const int pseg = (4 * sw + g) ^ pswz(tok);  // P segment of this lane's four heads in token row tok
 
-  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.0f;  // per head, same in its four lanes
+  float m_ref[4], m_raw[4], l_run[4];  // per output head: reference, running raw max, running sum
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m_ref[r] = -INFINITY;
+    m_raw[r] = -INFINITY;
+    l_run[r] = 0.0f;
+  }
   for (int pass = 0; pass < 2; ++pass) {
-    bool over = false;  // a score exceeded the reference by more than the headroom
     for (int n = 0; n <= bk.ntiles; ++n) {
       lds_barrier();  // tile n staged; P(n-2) consumed by the value waves
       if (!active || n >= bk.ntiles) continue;
-      // ---- S^T for tile n: lane holds head hl, tokens 4g + r
       const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
-      const int nin = min(kTT, bk.total - n * kTT);
-      const uint8_t* kr = tile + 16 * (lane & 15) + (lane >> 4) * kCS;
+      const uint8_t* kr = tile + 16 * tok + g * kCS;
       f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ks += 2) {
-        acc0 = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + 4 * ks * kCS), qv[ks], acc0);
-        acc1 = mfma16_bf16(*reinterpret_cast<const bf16x8*>(kr + 4 * (ks + 1) * kCS), qv[ks + 1], acc1);
+        acc0 = mfma16_bf16(qv[ks], *reinterpret_cast<const bf16x8*>(kr + 4 * ks * kCS), acc0);
+        acc1 = mfma16_bf16(qv[ks + 1], *reinterpret_cast<const bf16x8*>(kr + 4 * (ks + 1) * kCS), acc1);
       }
-      float pv[4];  // raw scores; cq > 0 scales them into log2 units below
+      float pv[4];  // raw scores of heads 4g + r; cq > 0 scales them into log2 units below
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = acc0[r] + acc1[r];
-      if (nin < kTT) {  // tail tile: entries past the end of the list get p = 0
+      if (tok >= bk.total - n * kTT) {  // tail tile: entries past the end of the list get p = 0
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r >= nin) pv[r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) pv[r] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3]));
-      mx = max4x16(mx) * cq;  // scaling by cq > 0 commutes with the max
-      m_max = fmaxf(m_max, mx);
-      m_ref = m_ref == -INFINITY ? mx : m_ref;
-      over |= mx > m_ref + kRefHeadroom;
-      float lsum = 0.0f;
-      const float nref = -m_ref;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m_raw[r] = __builtin_elementwise_maximum(m_raw[r], pv[r]);
+      if (pass == 0 && n == 0) {
+        // the reference of the first pass: each head's max over the first tile (scaling by
+        // cq > 0 commutes with the max)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m_ref[r] = max16(m_raw[r]) * cq;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = fast_exp2(fmaf(pv[r], cq, nref));
-        lsum += pv[r];
+        pv[r] = fast_exp2(fmaf(pv[r], cq, -m_ref[r]));
+        l_run[r] += pv[r];
       }
-      l_run += lsum;
-      // P = bf16(p) as [head][token]: this lane's tokens 4g .. 4g+3 of head hl
-      *reinterpret_cast<bf16x4*>(sh.pbuf + (n & 1) * kPTile + hl * kPRow + 8 * g) =
+      // P = bf16(p) as [token][head]: this lane's heads 16sw + 4g .. +3 of token tok
+      *reinterpret_cast<bf16x4*>(sh.pbuf + (n & 1) * kPTile + tok * kPRow + 8 * pseg) =
           bf16x4{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
     }
     // a second pass, with the exact max as reference, only if some score outgrew the headroom
+    bool over = false;
+    float m_max[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_max[r] = active ? max16(m_raw[r]) * cq : -INFINITY;
+      over |= m_max[r] > m_ref[r] + kRefHeadroom;
+    }
     if (!__syncthreads_or(over)) break;
-    m_ref = m_max;
-    l_run = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_ref[r] = m_max[r];
+      m_raw[r] = -INFINITY;
+      l_run[r] = 0.0f;
+    }
   }
 
   // ---- per-head (max, sum) for the value waves; lse or the split partial
   if (active) {
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const float mo = l_tot > 0.0f ? m_ref : -INFINITY;
-    if (g == 0) {
-      sh.ml[2 * hl] = mo;
-      sh.ml[2 * hl + 1] = l_tot;
-      const int head = bk.h_lo + hl;
-      if (p.splits == 1) {
-        p.lse[(int64_t)bk.row * p.l_st + (int64_t)head * p.l_sh] =
-            l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-      } else {
-        const int64_t pidx = ((int64_t)bk.row * p.splits + bk.split) * p.H + head;
-        p.ws_ml[pidx * 2 + 0] = mo;
-        p.ws_ml[pidx * 2 + 1] = l_tot;
+    float l_tot[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_tot[r] = sum16(l_run[r]);
+    if (tok == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * sw + 4 * g + r;
+        const float mo = l_tot[r] > 0.0f ? m_ref[r] : -INFINITY;
+        sh.ml[2 * h] = mo;
+        sh.ml[2 * h + 1] = l_tot[r];
+        const int head = bk.h_lo + h;
+        if (p.splits == 1) {
+          p.lse[(int64_t)bk.row * p.l_st + (int64_t)head * p.l_sh] =
+              l_tot[r] > 0.0f ? (m_ref[r] + __log2f(l_tot[r])) * kLn2 : -INFINITY;
+        } else {
+          const int64_t pidx = ((int64_t)bk.row * p.splits + bk.split) * p.H + head;
+          p.ws_ml[pidx * 2 + 0] = mo;
+          p.ws_ml[pidx * 2 + 1] = l_tot[r];
+        }
       }
     }
   }
@@ -188,6 +222,22 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, const Block& bk, int vw, int lane) {
   // O^T blocks o[db][hg]: dims 128vw + 32db + 8(r/4) + 4(lane/32) + r%4, head 32hg + lane%32
   f32x16 o[4][2];
+  // P^T operand of head block hg (heads 32hg + lane%32, tokens 8(lane/32) .. +7) as two
+  // transposed reads: in its 16-lane group G the lane a addresses token 8(G/2) + a/4 (then
+  // + 4) and heads H0 + 4(a%4) .. +3 (H0 = 32hg + 16(G%2)), and receives head H0 + a of the
+  // four tokens.  Offsets within a probability tile.
+  int poff[2][2];
+  {
+    const int G = lane >> 4, a = lane & 15;
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int tk = 8 * (G >> 1) + (a >> 2) + 4 * half;
+        const int seg = 8 * hg + 4 * (G & 1) + (a & 3);
+        poff[hg][half] = tk * kPRow + 8 * (seg ^ pswz(tk));
+      }
+  }
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -206,10 +256,13 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
       const int m = n - 1;
       const uint8_t* tile = sh.stage + (m % kStages) * kTileBytes;
       const uint8_t* pb = sh.pbuf + (m & 1) * kPTile;
-      const int h32 = lane & 31, lh = lane >> 5;
       bf16x8 pf[2];
 #pragma unroll
-      for (int hg = 0; hg < 2; ++hg) pf[hg] = *reinterpret_cast<const bf16x8*>(pb + (32 * hg + h32) * kPRow + 16 * lh);
+      for (int hg = 0; hg < 2; ++hg) {
+        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS i16x4*)(pb + poff[hg][0]));
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS i16x4*)(pb + poff[hg][1]));
+        pf[hg] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
       // tr16 source of this lane a (in its 16-lane group G = lane / 16): token 8(G/2) + a/4 (+4 for
       // the second read), dims D0 + 4(a%4) .. +3 with D0 = 128vw + 32db + 16(G%2)
       const int a = lane & 15, G = lane >> 4;
@@ -231,46 +284,7 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
     if (!__syncthreads_or(false)) break;
   }
   __syncthreads();  // the score waves' (max, sum) are in LDS
-
-  const int h32 = lane & 31;
-  const int dbase = 128 * vw + 4 * (lane >> 5);  // + 32db + 8qd
-#pragma unroll
-  for (int hg = 0; hg < 2; ++hg) {
-    const int hl = 32 * hg + h32;
-    if (hl >= bk.nh) continue;
-    const int head = bk.h_lo + hl;
-    if (p.splits == 1) {
-      const float lt = sh.ml[2 * hl + 1];
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      if (p.out_fp32) {
-        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * qd) =
-                f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
-      } else {
-        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)head * p.o_sh + dbase;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * qd) =
-                bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
-                       (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
-      }
-    } else {
-      // split-K: this split's unnormalised partial
-      float* po = p.ws_o + (((int64_t)bk.row * p.splits + bk.split) * p.H + head) * kLatent + dbase;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd) =
-              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]};
-    }
-  }
+  stage_output(p, sh.ml, staging(sh), o, vw, lane);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p) {
@@ -288,6 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p
     score_role(p, sh, bk, wave, lane);
   else
     value_role(p, sh, bk, wave - 4, lane);
+  __syncthreads();  // output rows staged
+  store_rows(p, bk, staging(sh), tid);
   if (p.splits == 1) return;
   if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, tid);
 }

@@ -8,6 +8,7 @@
 #include "smla_internal.h"
 
 #include <math.h>
+#include <stddef.h>
 
 namespace smla {
 namespace dec {
@@ -87,6 +88,108 @@ __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
   bk.h_lo = bk.hb * kHB;
   bk.nh = min(kHB, p.H - bk.h_lo);  // a multiple of 16
   return true;
+}
+
+// Probability tiles are [token][head] rows of 64 bf16 values (128 bytes) in 8-byte segments of
+// four heads; segment s of token j sits at segment s ^ pswz(j).  pswz swaps the two 2-bit
+// fields of j's low four bits, so both the score waves' stores (sixteen tokens, one segment
+// each) and the value waves' transposed reads (four tokens x four segments per 16-lane
+// group) touch sixteen distinct segments: no bank conflicts either way.
+__device__ __forceinline__ int pswz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
+
+// Max and sum over the 16 lanes of a lane group (lanes 16g .. 16g + 15); every lane of the
+// group gets the same result.
+__device__ __forceinline__ float max16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Output staging rows after a decode kernel's tile loop: 16 bytes of padding put consecutive
+// rows four banks apart, so the value waves' row-strided writes do not conflict.
+constexpr int kOutPitch32 = 4 * kLatent + 16;  // fp32 rows
+constexpr int kOutPitch16 = 2 * kLatent + 16;  // bf16 rows
+constexpr int kOutStageBytes = kHB * kOutPitch32;  // LDS span a kernel provides after its loop
+
+// Value wave vw's O^T blocks (o[db][hg]: dims 128vw + 32db + 8(r/4) + 4(lane/32) + r%4, head
+// 32hg + lane%32), normalised by the head's sum when the call has one split, into the staging
+// rows [head][dim] at stg: fp32 for split partials and fp32 outputs, bf16 otherwise.
+__device__ __forceinline__ void stage_output(const DecodeParams& p, const float* ml, uint8_t* stg,
+                                             const f32x16 (&o)[4][2], int vw, int lane) {
+  const bool f32out = p.splits > 1 || p.out_fp32;
+  const int h32 = lane & 31;
+  const int dbase = 128 * vw + 4 * (lane >> 5);  // + 32db + 8qd
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    const int hl = 32 * hg + h32;
+    float inv = 1.0f;
+    if (p.splits == 1) {
+      const float lt = ml[2 * hl + 1];
+      inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    }
+    if (f32out) {
+      float* r = reinterpret_cast<float*>(stg + hl * kOutPitch32) + dbase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(r + 32 * db + 8 * qd) =
+              f32x4{o[db][hg][4 * qd], o[db][hg][4 * qd + 1], o[db][hg][4 * qd + 2], o[db][hg][4 * qd + 3]} * inv;
+    } else {
+      __bf16* r = reinterpret_cast<__bf16*>(stg + hl * kOutPitch16) + dbase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<bf16x4*>(r + 32 * db + 8 * qd) =
+              bf16x4{(__bf16)(o[db][hg][4 * qd] * inv), (__bf16)(o[db][hg][4 * qd + 1] * inv),
+                     (__bf16)(o[db][hg][4 * qd + 2] * inv), (__bf16)(o[db][hg][4 * qd + 3] * inv)};
+    }
+  }
+}
+
+// Staged output rows -> global memory, 16 bytes per thread and 1 KB of one row per wave and
+// instruction (a direct store from the MFMA layout would touch 32 rows per instruction).
+// Rows of heads past the block's last head are not written.
+__device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& bk, const uint8_t* stg, int tid) {
+  if (p.splits > 1 || p.out_fp32) {
+    float* base;
+    int64_t hstride;
+    if (p.splits > 1) {  // this split's unnormalised partial
+      base = p.ws_o + ((int64_t)bk.row * p.splits + bk.split) * p.H * kLatent;
+      hstride = kLatent;
+    } else {
+      base = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st;
+      hstride = p.o_sh;
+    }
+    constexpr int kChunksPerRow = 4 * kLatent / 16;  // 128
+#pragma unroll
+    for (int k = 0; k < kHB * kChunksPerRow / kThreads; ++k) {
+      const int c = tid + kThreads * k;
+      const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
+      if (hl < bk.nh) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + hl * kOutPitch32 + 16 * col);
+        *reinterpret_cast<f32x4*>(base + (int64_t)(bk.h_lo + hl) * hstride + 4 * col) = v;
+      }
+    }
+  } else {
+    __bf16* base = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st;
+    constexpr int kChunksPerRow = 2 * kLatent / 16;  // 64
+#pragma unroll
+    for (int k = 0; k < kHB * kChunksPerRow / kThreads; ++k) {
+      const int c = tid + kThreads * k;
+      const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
+      if (hl < bk.nh) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(stg + hl * kOutPitch16 + 16 * col);
+        *reinterpret_cast<i32x4*>(base + (int64_t)(bk.h_lo + hl) * p.o_sh + 8 * col) = v;
+      }
+    }
+  }
 }
 
 // Compacts this split's slot entries that lie in [0, num_slots) into sh.clist, in order;
