@@ -169,3 +169,25 @@ def test_decode_late_dominant_score_exceeds_headroom(kv, splits):
                            num_splits=splits, kv_layout=kv)
     torch.cuda.synchronize()
     check_close(out, lse, ro, rl, what=f"late dominant {kv} splits {splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_query_ranges_per_head(splits):
+    """Heads of q scaled by powers of two from 2^-110 to 2^3, and one all-zero head: the
+    per-head range factor of the query split (2^e with max |q 2^e| near 448, clamped to
+    |e| <= 100) is taken back out by the fp8 MFMA's per-row scale, so every head must match."""
+    import dataclasses
+
+    w = make_random(91, T=5, H=64, K=300, ctx=700, B=64, neg_frac=0.1, n_req=2)
+    q = w.q_f32().copy()
+    exps = [-110, -30, -12, -4, 0, 3]
+    for h in range(w.H):
+        q[:, h, :] *= np.float32(2.0 ** exps[h % len(exps)])
+    q[:, 7, :] = 0.0
+    bits = q.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "power-of-two scaling keeps the values bf16"
+    w = dataclasses.replace(w, q_bits=(bits >> 16).astype(np.uint16))
+    print(f"decode query ranges splits={splits}", flush=True)
+    out, lse = gpu_decode(w, out_dtype=torch.float32, num_splits=splits)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what=f"q ranges s{splits}")
