@@ -44,6 +44,9 @@
 //  * Split-K over the top-k list with an in-kernel combine: every split writes its
 //    unnormalised partial (O, max, sum) to the workspace; the last split to arrive (device
 //    scope counter, zeroed by a small kernel before the decode kernel) merges them.
+//  * The output leaves through LDS: after the loop the value waves write O as [head][dim]
+//    rows into the freed tile, probability and slot-list buffers, and all eight waves store
+//    whole rows.
 //  * A row with no valid entry yields out = 0, lse = -inf.
 
 #include "decode_common.h"
