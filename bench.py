@@ -36,11 +36,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def decode_algorithmic(T, H, K, nvalid, out_bytes):
-    """Bytes and flops one decode launch must move / compute."""
-    byts = 656 * nvalid + T * H * 576 * 2 + T * K * 4 + T * H * (512 * out_bytes + 4)
+def decode_algorithmic(T, H, K, nvalid, nunique, out_bytes, record_bytes=656):
+    """Bytes and flops one decode launch must move / compute: every distinct record the launch
+    reads once (rows of one request that picked the same token share it), q, the slot lists,
+    out and LSE; 2176 flops per (valid id, head) of every row."""
+    byts = record_bytes * nunique + T * H * 576 * 2 + T * K * 4 + T * H * (512 * out_bytes + 4)
     flops = FLOP_PER_VALID_ID_PER_HEAD * H * nvalid
     return byts, flops
+
+
+def unique_records(ids, req, dcp_size=1, dcp_rank=0):
+    """Distinct valid ids per request that DCP rank `dcp_rank` owns (interleave 1), summed over
+    requests: the records one decode launch of that rank must read at least once."""
+    import numpy as np
+    ids, req = np.asarray(ids), np.asarray(req)
+    n = 0
+    for b in np.unique(req):
+        x = ids[req == b]
+        x = x[(x >= 0) & (x % dcp_size == dcp_rank)]
+        n += int(np.unique(x).size)
+    return n
 
 
 def roofline_entry(byts, flops, seconds):
@@ -216,8 +231,8 @@ def main_bf16(args):
     wall = time.perf_counter() - t0
     call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     nvalid = int((w.ids >= 0).sum())
-    byts = 1152 * nvalid + w.T * w.H * 576 * 2 + w.T * w.K * 4 + w.T * w.H * (512 * 2 + 4)
-    flops = FLOP_PER_VALID_ID_PER_HEAD * w.H * nvalid
+    byts, flops = decode_algorithmic(w.T, w.H, w.K, nvalid, unique_records(w.ids, w.req), out_bytes=2,
+                                     record_bytes=1152)
     roof = roofline_entry(byts, flops, call_s)
     roof.update({"traffic": None, "kernel": "decode_bf16_kernel (one unsharded call)", "launch_us": round(call_s * 1e6, 2),
                  "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
@@ -370,10 +385,11 @@ def main():
                          lse_layout="HT", device=dev)
     # valid ids per shard (host-side count from the inputs, outside any timed region)
     nvalid = [int((np.asarray(w.ids) >= 0).sum())]
-    shard_valid = []
+    shard_valid, shard_unique = [], []
     for r in range(w.dcp_size):
         own = (w.ids >= 0) & ((w.ids % w.dcp_size) == r)
         shard_valid.append(int(own.sum()))
+        shard_unique.append(unique_records(w.ids, w.req, w.dcp_size, r))
 
     decode_events = []  # (start, end) events around every decode launch, on the launch stream
     stream = torch.cuda.current_stream(dev)
@@ -404,7 +420,7 @@ def main():
     # decode kernel roofline: mean over the timed launches (both shards have ~the same valid count)
     mean_dec_s = float(np.mean(dec_ms)) / 1e3
     nv_mean = float(np.mean(shard_valid))
-    byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, out_bytes=4)
+    byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, float(np.mean(shard_unique)), out_bytes=4)
     roof = roofline_entry(byts, flops, mean_dec_s)
     roof["traffic"] = measured_traffic()
     roof["kernel"] = "decode_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
@@ -427,7 +443,7 @@ def main():
         torch.cuda.synchronize()
         un_ms = [a.elapsed_time(b) for a, b in un_events]
         un_s = float(np.mean(un_ms)) / 1e3
-        ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], out_bytes=2)
+        ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], unique_records(w.ids, w.req), out_bytes=2)
         unsharded = {"decode_us": round(un_s * 1e6, 2), "decode_us_p10_p50_p90": percentiles_us(un_ms),
                      "tflops": round(uf / un_s / 1e12, 1),
                      "kv_gbps": round(656 * nvalid[0] / un_s / 1e9, 1), "roofline": roofline_entry(ub, uf, un_s)}
