@@ -265,9 +265,10 @@ def main_bf16(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, budget_s):
-    """fp64 oracle of the same DCP2 step (converts, shard attention, merge) over the rows in
-    order, wrapping around, until the time budget is spent; rows/s over the rows done."""
+def cpu_baseline(w, budget_s, order=None, what=None):
+    """fp64 oracle of the same DCP step (converts, shard attention, merge) over the rows in
+    `order` (default: in order), wrapping around, until the time budget is spent; rows/s over
+    the rows done."""
     import numpy as np
     import oracle.smla_oracle as O
     try:
@@ -275,11 +276,12 @@ def cpu_baseline(w, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    order = list(range(w.T)) if order is None else [int(r) for r in order]
     rows_done, t0 = 0, time.perf_counter()
     chunk = 4
     while time.perf_counter() - t0 < budget_s:
-        start = rows_done % w.T
-        rows = list(range(start, min(w.T, start + chunk)))
+        start = rows_done % len(order)
+        rows = order[start:start + chunk]
         sub = w.rows(rows)
         q = sub.q_f32()
         outs, lses = [], []
@@ -292,9 +294,9 @@ def cpu_baseline(w, budget_s):
         rows_done += len(rows)
     dt = time.perf_counter() - t0
     return {"value": round(rows_done / dt, 3), "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} rows (the {w.T} rows of the same DCP2 step in order, wrapping) through the fp64 "
-                      f"numpy oracle: 2 shard converts, shard attention, LSE merge; {dt:.1f} s on "
-                      f"{os.cpu_count()} host CPUs"}
+            "sample": f"{rows_done} rows ({what or f'the {w.T} rows of the same DCP{w.dcp_size} step in order'}, "
+                      f"wrapping) through the fp64 numpy oracle: {w.dcp_size} shard converts, shard attention, LSE "
+                      f"merge; {dt:.1f} s on {os.cpu_count()} host CPUs"}
 
 
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
@@ -328,6 +330,74 @@ def percentiles_us(ms):
     return [round(float(x) * 1e3, 2) for x in np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])]
 
 
+def main_c4(args):
+    """--workload c4: the long-context mixed batch (128 decode rows with 131072-token contexts
+    and 4096 prefill rows of two fresh 2048-token prompts, T = 4224, H = 128, top-k 2048),
+    simulated DCP8: per step 8 x (convert + decode into fp32 partials) and one LSE merge."""
+    import numpy as np
+    import torch
+    import sparse_mla_decode_topk_amd as smla
+    from sparse_mla_decode_topk_amd.pipeline import DcpDecodeStep, device_shards
+    from workload import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    smla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log("generating workload c4 (T=4224, H=128, top-k 2048, decode ctx 131072, DCP8) ...")
+    t0 = time.perf_counter()
+    w = make_config(4)
+    log(f"  generated in {time.perf_counter() - t0:.1f} s; copying the 8 shard caches to the GPU")
+    q = w.q_torch().to(dev)
+    ids = torch.from_numpy(w.ids).to(dev)
+    req = torch.from_numpy(w.req).to(dev)
+    shards = device_shards(w, dev)  # one copy: 8 x 1.4 GB of shard caches, far beyond the 256 MB MALL
+    torch.cuda.synchronize()
+    step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=w.dcp_size, block_size=w.block_size,
+                         softmax_scale=w.sm_scale, out_dtype=torch.bfloat16, partial_dtype=torch.float32,
+                         lse_layout="HT", device=dev)
+    shard_valid = [int(((w.ids >= 0) & (w.ids % w.dcp_size == r)).sum()) for r in range(w.dcp_size)]
+    shard_unique = [unique_records(w.ids, w.req, w.dcp_size, r) for r in range(w.dcp_size)]
+    stream = torch.cuda.current_stream(dev)
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step.run(q, ids, req, shards)
+    torch.cuda.synchronize()
+    decode_events = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(q, ids, req, shards, decode_events=decode_events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    dec_ms = [a.elapsed_time(b) for a, b in decode_events]
+    mean_dec_s = float(np.mean(dec_ms)) / 1e3
+    byts, flops = decode_algorithmic(w.T, w.H, w.K, float(np.mean(shard_valid)), float(np.mean(shard_unique)),
+                                     out_bytes=4)
+    roof = roofline_entry(byts, flops, mean_dec_s)
+    roof.update({"traffic": None,
+                 "kernel": "decode_kernel (one DCP8 shard call: T=4224, H=128, K=2048, fp32 partials)",
+                 "launch_us": round(mean_dec_s * 1e6, 2), "launch_us_p10_p50_p90": percentiles_us(dec_ms),
+                 "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
+                 "mfma_frac": round(flops / mean_dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)})
+    line = {
+        "metric": METRIC, "value": round(w.T * args.steps / wall, 1), "unit": "query-rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "c4_mixed_dcp8: 128 decode rows (ctx 131072) + 4096 prefill rows (2 x 2048), "
+                               "H=128, top-k 2048, fp8_ds_mla cache, simulated DCP8 (convert+decode per shard, "
+                               "LSE merge)",
+                   "T": w.T, "H": w.H, "topk": w.K, "dcp": w.dcp_size, "block_size": w.block_size},
+        "kv_gbps": round(656 * sum(shard_valid) * args.steps / (float(np.sum(dec_ms)) / 1e3) / 1e9, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        order = np.random.Generator(np.random.PCG64(4004)).permutation(w.T)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, order=order,
+                                            what=f"the {w.T} rows of the DCP8 step in a seeded random order")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,9 +408,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unsharded", action="store_true",
                     help="skip the unsharded decode of the same rows (timed after the step and reported beside it)")
-    ap.add_argument("--workload", choices=("c3", "dense", "bf16"), default="c3",
+    ap.add_argument("--workload", choices=("c3", "dense", "bf16", "c4"), default="c3",
                     help="c3: the DCP2 MTP step (default); dense: the whole-context MTP decode; bf16: the c3 rows "
-                         "unsharded against a plain bf16 cache")
+                         "unsharded against a plain bf16 cache; c4: the long-context mixed batch under DCP8")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -353,6 +423,9 @@ def main():
         return
     if args.workload == "bf16":
         main_bf16(args)
+        return
+    if args.workload == "c4":
+        main_c4(args)
         return
 
     import numpy as np
