@@ -157,10 +157,31 @@ __device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, con
   return p.kv + (int64_t)sh.clist[idx] * kRecordBytes + 16 * (lane >> 5);
 }
 
+// A score wave lane's query values as loaded: latent dims 128t + 32g + 8c .. +7 in lat[4t + c]
+// and rope dims 32kk + 8g .. +7 in rope[kk] (g = lane >> 4), bf16 bits.
+struct QRaw {
+  i32x4 lat[16];
+  i32x4 rope[2];
+};
+
+// Issued before the slot compaction, so the query and slot-list loads share one memory round
+// trip.
+__device__ __forceinline__ void load_q(const DecodeParams& p, const Block& bk, int sw, int lane, QRaw& qv) {
+  const int g = lane >> 4;
+  const uint16_t* qp = p.q + (int64_t)bk.row * p.q_st + (int64_t)(bk.h_lo + 16 * sw + (lane & 15)) * p.q_sh;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qv.lat[4 * t + c] = *reinterpret_cast<const i32x4*>(qp + 128 * t + 32 * g + 8 * c);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) qv.rope[kk] = *reinterpret_cast<const i32x4*>(qp + kLatent + 32 * kk + 8 * g);
+}
+
 // ---------------------------------------------------------------------------------------
 // Score wave `sw` (0..3): heads h_lo + 16sw + (lane & 15); lane group g = lane >> 4 holds
 // the query dims 128t + 32g .. +31 of every scale tile t and rope dims 32kk + 8g .. +7.
-__device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, const Block& bk, int sw, int lane) {
+__device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, const Block& bk, const QRaw& qv,
+                                           int sw, int lane) {
   const int g = lane >> 4;
   const int hl = 16 * sw + (lane & 15);  // head within the block
   const bool active = 16 * sw < bk.nh;
@@ -168,7 +189,6 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
   bf16x8 qr[2];        // rope q (bf16 as given): element i of kk <-> rope dim 32kk + 8g + i
   int qsa = kUnitScale;  // E8M0 of 2^-e: the latent MFMAs scale q's rows back by it
   if (active) {
-    const uint16_t* qp = p.q + (int64_t)bk.row * p.q_st + (int64_t)(bk.h_lo + hl) * p.q_sh;
     // pass 1: per-head max |q| over the latent dims (the rope dims are used as given), as an
     // integer max of the bf16 magnitude bits, two values per instruction (lanes l, l^16, l^32,
     // l^48 hold one head)
@@ -178,7 +198,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(qp + 128 * t + 32 * g + 8 * c);
+        const i32x4 v = qv.lat[4 * t + c];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           mbits = __builtin_elementwise_max(mbits, __builtin_bit_cast(u16x2, (uint32_t)v[i] & 0x7FFF7FFFu));
@@ -198,7 +218,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 128 * t + 32 * g + 8 * c);
+        const bf16x8 v = __builtin_bit_cast(bf16x8, qv.lat[4 * t + c]);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           int hi, lo;
@@ -210,7 +230,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      qr[kk] = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 * kk + 8 * g);
+      qr[kk] = __builtin_bit_cast(bf16x8, qv.rope[kk]);
     }
   } else {
     // an idle score wave (fewer than 64 heads) keeps its heads' probability segments at zero
@@ -425,12 +445,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
   Block bk;
   if (!block_of(p, bk)) return;
+  QRaw qv;
+  if (wave < 4 && 16 * wave < bk.nh) load_q(p, bk, wave, lane, qv);
   bk.total = compact_slots(p, bk, sh, tid, wave, lane);
   bk.ntiles = (bk.total + kTT - 1) / kTT;
 
   // The two roles run the same number of workgroup barriers, one per loop step.
   if (wave < 4)
-    score_role(p, sh, bk, wave, lane);
+    score_role(p, sh, bk, qv, wave, lane);
   else
     value_role(p, sh, bk, wave - 4, lane);
   __syncthreads();  // output rows staged
