@@ -302,8 +302,8 @@ def cpu_baseline(w, budget_s, order=None, what=None):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "886f6477b4de61b929936fc3af53878db05cdcf7ec932803a2d727998dd0914a",
-                  "fetch_bytes": 227759008, "write_bytes": 67241440}
+DECODE_TRAFFIC = {"sources_sha256": "bbdc796c688f3535c22f0a321bc7c1ef84caac3e6da2cd6865d61d3a9c7e8a18",
+                  "fetch_bytes": 227235936, "write_bytes": 67241240}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
