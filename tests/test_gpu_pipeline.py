@@ -87,6 +87,23 @@ def test_dcp8_c4_subset_rows_full_caches():
     print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
 
 
+def test_dcp8_c4_full_size_sampled():
+    """The mixed batch at its full size (T = 4224, 8 shards), in the launch the c4 bench line times;
+    sampled rows against the oracle: decode rows, and prefill rows at positions 0-9 (a row at position
+    p has p + 1 candidates, so up to 7 of its 8 shards own none and must drop out of the merge) and
+    further along both prompts."""
+    w = make_config(4)
+    print(f"c4 full: T={w.T} H={w.H} D={w.dcp_size}", flush=True)
+    step, out, lse = run_step(w, lse_layout="HT")
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    pos = np.asarray(w.row_pos)
+    short = [int(r) for r in np.flatnonzero(pos < 10)]
+    rows = sorted(set(range(0, w.T, 101)) | set(short) | {w.T - 1})
+    ref_o, ref_l = oracle_unsharded(w, rows)
+    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, what="c4 sampled rows")
+    print(f"  {len(rows)} sampled rows max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("S,dtype", [(1, torch.float32), (2, torch.float32), (4, torch.bfloat16), (8, torch.float32)])
 def test_merge_against_oracle(S, dtype):
     rng = np.random.default_rng(S)
