@@ -191,3 +191,23 @@ def test_decode_query_ranges_per_head(splits):
     out, lse = gpu_decode(w, out_dtype=torch.float32, num_splits=splits)
     ref_o, ref_l = oracle_unsharded(w)
     check_close(out, lse, ref_o, ref_l, what=f"q ranges s{splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 3, 5])
+def test_decode_list_longer_than_one_workgroup(splits):
+    """K = 9000 exceeds the 4096 slot entries one workgroup compacts: the call splits the list
+    itself (at least three ranges), or takes the forced count when that is enough."""
+    w = make_random(97, T=3, H=64, K=9000, ctx=20000, B=64, neg_frac=0.05, n_req=1)
+    print(f"decode K=9000 splits={splits}", flush=True)
+    out, lse = gpu_decode(w, out_dtype=torch.float32, num_splits=splits)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what=f"K9000 s{splits}")
+
+
+def test_decode_longest_list():
+    """The longest list a call takes: 64 ranges of 4096 entries (K = 262144), one row, 16 heads."""
+    w = make_random(98, T=1, H=16, K=262144, ctx=262244, B=64, neg_frac=0.05, n_req=1)
+    print("decode K=262144", flush=True)
+    out, lse = gpu_decode(w, out_dtype=torch.float32)
+    ref_o, ref_l = oracle_unsharded(w)
+    check_close(out, lse, ref_o, ref_l, what="K262144")

@@ -39,7 +39,7 @@ def test_bf16_c0():
 
 
 @pytest.mark.parametrize("H,K,neg", [(16, 48, 0.0), (64, 300, 0.3), (128, 2048, 0.1), (32, 17, 0.0),
-                                     (128, 4096, 0.5)])
+                                     (128, 4096, 0.5), (32, 9000, 0.05)])
 def test_bf16_random_shapes(H, K, neg):
     w = make_random(500 + H + K, T=9, H=H, K=K, ctx=max(K, 64) + 40, B=16, neg_frac=neg, n_req=3, kv="bf16")
     print(f"bf16 random: T={w.T} H={H} K={K} neg={neg}", flush=True)

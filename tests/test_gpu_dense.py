@@ -30,10 +30,11 @@ CASES = [
     dict(seed=1, n_req=3, S=2, H=32, ctx=[300, 37, 1], B=16),
     dict(seed=2, n_req=4, S=4, H=128, ctx=[2100, 700, 64, 3], B=64),  # a row list longer than one split
     dict(seed=3, n_req=2, S=1, H=16, ctx=[129, 0], B=32),  # plain decode, and an empty request
+    dict(seed=4, n_req=2, S=1, H=16, ctx=[10000, 4097], B=64),  # lists longer than one workgroup compacts
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"S{c['S']}H{c['H']}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c['seed']}S{c['S']}H{c['H']}")
 def test_dense_unsharded(case):
     c = dict(case)
     S = c["S"]
