@@ -150,11 +150,13 @@ __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* rec, i
   }
 }
 
-// Record of tile entry (lane & 31); entries past the end of the list repeat the last one.
-__device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, const Shared& sh, int n, int total,
-                                                      int lane) {
-  const int idx = min(n * kTT + (lane & 31), total - 1);
-  return p.kv + (int64_t)sh.clist[idx] * kRecordBytes + 16 * (lane >> 5);
+// Slot of tile entry (lane & 31); entries past the end of the list repeat the last one.
+__device__ __forceinline__ int lane_slot(const Shared& sh, int n, int total, int lane) {
+  return sh.clist[min(n * kTT + (lane & 31), total - 1)];
+}
+// This lane's 16-byte column of that slot's record.
+__device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, int slot, int lane) {
+  return p.kv + (int64_t)slot * kRecordBytes + 16 * (lane >> 5);
 }
 
 // A score wave lane's query values as loaded: latent dims 128t + 32g + 8c .. +7 in lat[4t + c]
@@ -260,16 +262,17 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       const uint8_t* tile = sh.stage + (n % kStages) * kTileBytes;
       const int nin = min(kTT, bk.total - n * kTT);
       f32x4 s[2];
+      // every operand of the tile is read from LDS first, in the order the MFMAs use them
+      bf16x8 rb[2][2];
+      i32x4 kb[4][2][2];
+      f32x4 sc[2];  // [hf]: the four tile scales of token 16hf + tok
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const uint8_t* kr = tile + 16 * (16 * hf + tok);
-        f32x4 acc = {};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          acc = mfma16_bf16(qr[kk], *reinterpret_cast<const bf16x8*>(kr + (kRopeChunk + 4 * kk + g) * kCS), acc);
-        s[hf] = acc;
+          rb[hf][kk] = *reinterpret_cast<const bf16x8*>(kr + (kRopeChunk + 4 * kk + g) * kCS);
       }
-      f32x4 sc[2];  // [hf]: the four tile scales of token 16hf + tok
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         sc[hf] = *reinterpret_cast<const f32x4*>(tile + kScaleChunk * kCS + 16 * (16 * hf + tok));
@@ -278,8 +281,24 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const uint8_t* kr = tile + 16 * (16 * hf + tok) + (8 * t + 2 * g) * kCS;
-          const i32x4 a0 = *reinterpret_cast<const i32x4*>(kr);
-          const i32x4 a1 = *reinterpret_cast<const i32x4*>(kr + kCS);
+          kb[t][hf][0] = *reinterpret_cast<const i32x4*>(kr);
+          kb[t][hf][1] = *reinterpret_cast<const i32x4*>(kr + kCS);
+        }
+      // keep all the reads ahead of the MFMAs: the scheduler would otherwise reuse a few operand
+      // registers and wait out one LDS round trip per scale tile
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) acc = mfma16_bf16(qr[kk], rb[hf][kk], acc);
+        s[hf] = acc;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const i32x4 a0 = kb[t][hf][0], a1 = kb[t][hf][1];
           const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
           f32x4 acc = mfma16_fp8(qh[t], a, f32x4{}, qsa);
           acc = mfma16_fp8(ql[t], a, acc, qsa);
@@ -390,13 +409,17 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, Shared& sh, co
 #pragma unroll
       for (int hg = 0; hg < 2; ++hg) o[db][hg] = f32x16{};
     for (int n = 0; n < kAhead && n < bk.ntiles; ++n)
-      issue_tile(sh.stage + n * kTileBytes, lane_record(p, sh, n, bk.total, lane), vw, lane);
+      issue_tile(sh.stage + n * kTileBytes, lane_record(p, lane_slot(sh, n, bk.total, lane), lane), vw, lane);
+    // the slot of the next tile to copy is read one step early, so its LDS round trip is
+    // hidden behind the PV work instead of sitting between the barrier and the copy
+    int next_slot = kAhead < bk.ntiles ? lane_slot(sh, kAhead, bk.total, lane) : 0;
     for (int n = 0; n <= bk.ntiles; ++n) {
       wait_tile(min(kAhead - 1, max(bk.ntiles - 1 - n, 0)), vw);  // tile n is in
       lds_barrier();  // tile n staged; P'(n-1) written; tile n-2 and P'(n-2) consumed
-      if (n + kAhead < bk.ntiles)
-        issue_tile(sh.stage + ((n + kAhead) % kStages) * kTileBytes, lane_record(p, sh, n + kAhead, bk.total, lane),
-                   vw, lane);
+      if (n + kAhead < bk.ntiles) {
+        issue_tile(sh.stage + ((n + kAhead) % kStages) * kTileBytes, lane_record(p, next_slot, lane), vw, lane);
+        if (n + kAhead + 1 < bk.ntiles) next_slot = lane_slot(sh, n + kAhead + 1, bk.total, lane);
+      }
       if (n == 0) continue;
       // ---- O^T += V^T P'^T for tile n-1
       const int m = n - 1;
