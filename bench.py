@@ -302,8 +302,8 @@ def cpu_baseline(w, budget_s, order=None, what=None):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "d60e632a6abf52e97445c1e6787986f4aafd6c660a4586dbcfe35f46f54102c4",
-                  "fetch_bytes": 227239408, "write_bytes": 67240984}
+DECODE_TRAFFIC = {"sources_sha256": "a5d49d7ba7b4d1c7b63335d8cbdd7e55b3ff5cef3a5d8873848efa7602791230",
+                  "fetch_bytes": 227251920, "write_bytes": 67315648}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 

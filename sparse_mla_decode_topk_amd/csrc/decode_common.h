@@ -155,7 +155,9 @@ __device__ __forceinline__ void stage_output(const DecodeParams& p, const float*
 
 // Staged output rows -> global memory, 16 bytes per thread and 1 KB of one row per wave and
 // instruction (a direct store from the MFMA layout would touch 32 rows per instruction).
-// Rows of heads past the block's last head are not written.
+// Rows of heads past the block's last head are not written.  The stores are non-temporal:
+// nothing in the kernel reads the output again, and streaming it past L2 leaves the L2
+// lines of the records to the other head block of the row.
 __device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& bk, const uint8_t* stg, int tid) {
   if (p.splits > 1 || p.out_fp32) {
     float* base;
@@ -174,7 +176,7 @@ __device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& b
       const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
       if (hl < bk.nh) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stg + hl * kOutPitch32 + 16 * col);
-        *reinterpret_cast<f32x4*>(base + (int64_t)(bk.h_lo + hl) * hstride + 4 * col) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(base + (int64_t)(bk.h_lo + hl) * hstride + 4 * col));
       }
     }
   } else {
@@ -186,7 +188,7 @@ __device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& b
       const int hl = c / kChunksPerRow, col = c % kChunksPerRow;
       if (hl < bk.nh) {
         const i32x4 v = *reinterpret_cast<const i32x4*>(stg + hl * kOutPitch16 + 16 * col);
-        *reinterpret_cast<i32x4*>(base + (int64_t)(bk.h_lo + hl) * p.o_sh + 8 * col) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(base + (int64_t)(bk.h_lo + hl) * p.o_sh + 8 * col));
       }
     }
   }
