@@ -162,7 +162,7 @@ def main_dense(args):
     call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     byts, flops = dense_algorithmic(w)
     roof = roofline_entry(byts, flops, call_s)
-    roof.update({"traffic": None, "kernel": "dense_slots_kernel + decode_kernel (one whole-context decode call)",
+    roof.update({"traffic": None, "kernel": "dense_slots_kernel + decode_row_kernel (one whole-context decode call)",
                  "launch_us": round(call_s * 1e6, 2), "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops)})
     line = {
         "metric": METRIC, "value": round(w.T * args.steps / wall, 1), "unit": "query-rows/s", "n_gpus": 1,
@@ -304,7 +304,7 @@ def cpu_baseline(w, budget_s, order=None, what=None):
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
 DECODE_TRAFFIC = {"sources_sha256": "a5d49d7ba7b4d1c7b63335d8cbdd7e55b3ff5cef3a5d8873848efa7602791230",
                   "fetch_bytes": 227251920, "write_bytes": 67315648}
-KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
+KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode_row.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
 
@@ -375,7 +375,7 @@ def main_c4(args):
                                      out_bytes=4)
     roof = roofline_entry(byts, flops, mean_dec_s)
     roof.update({"traffic": None,
-                 "kernel": "decode_kernel (one DCP8 shard call: T=4224, H=128, K=2048, fp32 partials)",
+                 "kernel": "decode_row_kernel (one DCP8 shard call: T=4224, H=128, K=2048, fp32 partials)",
                  "launch_us": round(mean_dec_s * 1e6, 2), "launch_us_p10_p50_p90": percentiles_us(dec_ms),
                  "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
                  "mfma_frac": round(flops / mean_dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)})
@@ -496,7 +496,7 @@ def main():
     byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, float(np.mean(shard_unique)), out_bytes=4)
     roof = roofline_entry(byts, flops, mean_dec_s)
     roof["traffic"] = measured_traffic()
-    roof["kernel"] = "decode_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
+    roof["kernel"] = "decode_row_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
     roof["launch_us"] = round(mean_dec_s * 1e6, 2)
     roof["launch_us_p10_p50_p90"] = percentiles_us(dec_ms)
     roof["algorithmic_bytes"] = int(byts)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 2
+#define SMLA_ABI_VERSION 3
 
 enum smla_status {
   SMLA_OK = 0,
@@ -87,8 +87,9 @@ const char* smla_status_string(int status);
  * block_table [bt_rows, bt_ld] int32 (the shard's own table when dcp_size > 1);
  * slots [T, >=K] int32 output; slots may be topk_ids itself when slots_ld == ids_ld.
  * With K = 0 the index pointers may be NULL; only valid_count (zeros) is written.
- * Requirements: T, K >= 0; block_size >= 1; dcp_size >= 1; 0 <= dcp_rank < dcp_size;
- * interleave >= 1; ids_ld, slots_ld >= K; bt_ld >= bt_width >= 1; bt_rows >= 1;
+ * Requirements: T, K >= 0; block_size >= 1; dcp_size >= 1; dcp_rank >= 0; interleave >= 1;
+ * ids_ld, slots_ld >= K; bt_ld >= bt_width >= 1; bt_rows >= 1 (else SMLA_ERR_INVALID_ARG);
+ * dcp_rank < dcp_size (else SMLA_ERR_UNSUPPORTED: no such rank in the group);
  * int32 pointers 4-byte aligned (packed index arrays may be only 4-byte aligned,
  * [P-Stab] "Root causes and fixes", "PCP+DCP first-request JIT keys").
  */
@@ -129,6 +130,11 @@ size_t sparse_mla_decode_workspace_size(int32_t T, int32_t H, int32_t K, int32_t
  *          q, q_stride_t and q_stride_h*2 bytes must keep every head 16-byte aligned.
  * kv_cache [num_slots, 656] bytes, 16-byte aligned.
  * slots    int32 [T, >=K], 4-byte aligned (output of sparse_mla_convert_index).
+ * valid_count  int32 [T] or NULL, 4-byte aligned: the per-row counts sparse_mla_convert_index
+ *          returns ([P-SM120] "Summary": valid counts passed to the launcher as per-token
+ *          lengths).  A row whose count is <= 0 is written as out = 0, lse = -inf without
+ *          reading its q or its slots (the empty-row mask taken from the conversion,
+ *          [P-FlashMLA] "Review highlights"); any other count is not used, the slots decide.
  * out      [T, H, 512] bf16 (out_dtype SMLA_BF16) or fp32 (SMLA_FP32) at
  *          out + t*out_stride_t + h*out_stride_h, dims contiguous, 16-byte aligned rows.
  * lse      fp32 at lse + t*lse_stride_t + h*lse_stride_h: (T,H) layout with strides
@@ -145,8 +151,9 @@ size_t sparse_mla_decode_workspace_size(int32_t T, int32_t H, int32_t K, int32_t
  * always satisfy this); softmax_scale finite and > 0.
  */
 int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
-                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
-                      int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
+                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,
+                      int32_t T, int32_t H, int32_t K, float softmax_scale, void* out, int32_t out_dtype,
+                      int64_t out_stride_t,
                       int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
                       int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -165,8 +172,9 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
  * the errors are those of sparse_mla_decode.
  */
 int sparse_mla_decode_bf16(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
-                           int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
-                           int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
+                           int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,
+                           int32_t T, int32_t H, int32_t K, float softmax_scale, void* out, int32_t out_dtype,
+                           int64_t out_stride_t,
                            int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
                            int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -227,7 +235,8 @@ size_t sparse_mla_dense_decode_workspace_size(int32_t B, int32_t S, int32_t H, i
  * workspace at least sparse_mla_dense_decode_workspace_size(B, S, H, max_seq_len,
  *           dcp_size, interleave) bytes, 256-byte aligned; never NULL when B*S > 0.
  * Supported: the slot-list width (max_seq_len, or the rank-0 share of it under DCP) up to
- * 262144 (64 splits of 4096 entries); H as in sparse_mla_decode.
+ * 262144 (64 splits of 4096 entries); H as in sparse_mla_decode; dcp_rank < dcp_size
+ * (else SMLA_ERR_UNSUPPORTED).
  */
 int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
                             int64_t num_slots, const int32_t* block_table, int64_t bt_ld, int32_t bt_rows,
@@ -277,7 +286,8 @@ int sparse_mla_cache_write(const void* latent, int64_t latent_stride, const void
  * = (L / (I*D)) * I + clamp(L % (I*D) - dcp_rank*I, 0, I), 0 for L <= 0.
  * [P-Stab] "Root causes and fixes", "DCP decode rank scalar" (get_dcp_local_seq_lens;
  * the rank travels as a kernel argument, so no per-call device scalar is built).
- * seq_lens, local_seq_lens: int32 [R], 4-byte aligned.
+ * seq_lens, local_seq_lens: int32 [R], 4-byte aligned.  dcp_rank >= dcp_size (or
+ * dcp_size * interleave > 2^30) gives SMLA_ERR_UNSUPPORTED.
  */
 int sparse_mla_dcp_local_seq_lens(const int32_t* seq_lens, int32_t R, int32_t dcp_size, int32_t dcp_rank,
                                   int32_t interleave, int32_t* local_seq_lens, hipStream_t stream);

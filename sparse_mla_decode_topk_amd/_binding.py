@@ -60,8 +60,8 @@ def load_library():
         lib.sparse_mla_decode_workspace_size.restype = _SZ
         lib.sparse_mla_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
         lib.sparse_mla_decode.restype = ctypes.c_int
-        lib.sparse_mla_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _F32, _P, _I32, _I64,
-                                          _I64, _P, _I64, _I64, _I32, _P, _SZ, _P]
+        lib.sparse_mla_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _I32,
+                                          _I64, _I64, _P, _I64, _I64, _I32, _P, _SZ, _P]
         lib.sparse_mla_decode_bf16.restype = ctypes.c_int
         lib.sparse_mla_decode_bf16.argtypes = lib.sparse_mla_decode.argtypes
         lib.sparse_mla_merge_lse.restype = ctypes.c_int
@@ -173,25 +173,30 @@ _ws_cache = {}
 
 
 def workspace_for(T: int, H: int, K: int, device, num_splits: int = 0) -> Optional[torch.Tensor]:
-    """A per-device workspace at least as large as the call needs (cached and grown outside the
-    hot path; the library itself never allocates)."""
+    """A workspace at least as large as the call needs, cached per (device, stream) and grown outside
+    the hot path (the library itself never allocates).  Calls on one stream are ordered, so they may
+    share a workspace; a call on another stream gets its own, and a replaced buffer is released on the
+    stream that used it (the caching allocator orders its reuse after that stream's work)."""
     need = sparse_mla_decode_workspace_size(T, H, K, num_splits)
     if need == 0:
         return None
     device = torch.device(device)
-    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    stream = torch.cuda.current_stream(index)
+    key = (index, stream.cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=torch.device("cuda", index))
         _ws_cache[key] = ws
     return ws
 
 
 def convert_index(topk_ids: torch.Tensor, req_id_per_token: torch.Tensor, block_table: torch.Tensor,
                   block_size: int, dcp_size: int = 1, dcp_rank: int = 0, interleave: int = 1,
-                  out: Optional[torch.Tensor] = None, with_valid_count: bool = True
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Global top-k ids [T,K] -> slots [T,K] (and per-row valid counts [T])."""
+                  out: Optional[torch.Tensor] = None, with_valid_count: bool = True,
+                  valid: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Global top-k ids [T,K] -> slots [T,K] (and per-row valid counts [T], written into ``valid``
+    when given)."""
     _need(topk_ids, "topk_ids", torch.int32, 2)
     _need(req_id_per_token, "req_id_per_token", torch.int32, 1)
     _need(block_table, "block_table", torch.int32, 2)
@@ -206,7 +211,12 @@ def convert_index(topk_ids: torch.Tensor, req_id_per_token: torch.Tensor, block_
     _need(out, "out", torch.int32, 2)
     if tuple(out.shape) != (T, K) or (K > 1 and out.stride(1) != 1):
         raise ValueError("out must be [T,K] with a contiguous last dimension")
-    valid = torch.empty((T,), dtype=torch.int32, device=topk_ids.device) if with_valid_count else None
+    if valid is not None:
+        _need(valid, "valid", torch.int32, 1)
+        if valid.shape[0] != T or (T > 1 and valid.stride(0) != 1):
+            raise ValueError("valid must be a contiguous [T] int32 tensor")
+    elif with_valid_count:
+        valid = torch.empty((T,), dtype=torch.int32, device=topk_ids.device)
     R, W = block_table.shape
     st = sparse_mla_convert_index(
         topk_ids.data_ptr(), _st(topk_ids, 0), req_id_per_token.data_ptr(), block_table.data_ptr(),
@@ -222,9 +232,11 @@ KV_LAYOUTS = {"fp8_ds_mla": RECORD_BYTES, "bf16": 2 * HEAD_DIM}
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax_scale: float,
            out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
            lse: Optional[torch.Tensor] = None, lse_layout: str = "TH", num_splits: int = 0,
-           workspace: Optional[torch.Tensor] = None, kv_layout: str = "fp8_ds_mla") -> Tuple[torch.Tensor, torch.Tensor]:
+           workspace: Optional[torch.Tensor] = None, kv_layout: str = "fp8_ds_mla",
+           valid_count: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Sparse MLA decode.  q [T,H,576] bf16, kv_cache [num_slots,656] uint8 (kv_layout "fp8_ds_mla")
-    or [num_slots,1152] (kv_layout "bf16": 576 bf16 values per token), slots [T,K] int32.
+    or [num_slots,1152] (kv_layout "bf16": 576 bf16 values per token), slots [T,K] int32,
+    valid_count [T] int32 or None (the conversion's per-row counts: a row counted <= 0 is empty).
 
     Returns out [T,H,512] (out_dtype) and lse.  lse_layout "TH" gives a [T,H] tensor;
     "HT" writes the kernel-native [H,T] layout and returns its [T,H] transposed view.
@@ -244,6 +256,10 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax
     if slots.shape[0] != T or (K > 1 and slots.stride(1) != 1):
         raise ValueError("slots must be [T,K] with a contiguous last dimension")
     dev = q.device
+    if valid_count is not None:
+        _need(valid_count, "valid_count", torch.int32, 1)
+        if valid_count.shape[0] != T or (T > 1 and valid_count.stride(0) != 1):
+            raise ValueError("valid_count must be a contiguous [T] int32 tensor")
     if out is None:
         out = torch.empty((T, H, LATENT_DIM), dtype=out_dtype, device=dev)
     _need(out, "out", out.dtype, 3)
@@ -269,7 +285,8 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax
     call = sparse_mla_decode if kv_layout == "fp8_ds_mla" else sparse_mla_decode_bf16
     st = call(
         q.data_ptr(), _st(q, 0), _st(q, 1), kv_cache.data_ptr(), kv_cache.shape[0], slots.data_ptr(),
-        _st(slots, 0), T, H, K, float(softmax_scale), out.data_ptr(), _dtype_code(out.dtype), _st(out, 0),
+        _st(slots, 0), valid_count.data_ptr() if valid_count is not None else None, T, H, K, float(softmax_scale),
+        out.data_ptr(), _dtype_code(out.dtype), _st(out, 0),
         _st(out, 1), lse.data_ptr(), _st(lse, 0), _st(lse, 1), num_splits, ws_ptr, ws_bytes, _stream(dev))
     _check(call.__name__, st)
     return out, lse

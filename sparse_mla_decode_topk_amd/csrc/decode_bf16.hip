@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   Block bk;
-  if (!block_of(p, bk)) return;
+  if (!block_of(p, bk) || skip_marked_empty<kThreads>(p, bk, tid)) return;
   bk.total = compact_slots(p, bk, sh, tid, wave, lane);
   bk.ntiles = (bk.total + kTT - 1) / kTT;
 
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p
   __syncthreads();  // output rows staged
   store_rows(p, bk, staging(sh), tid);
   if (p.splits == 1) return;
-  if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, tid);
+  if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, reinterpret_cast<float*>(sh.stage), tid);
 }
 
 __global__ void zero_counters_bf16(int32_t* cnt, int64_t n) {

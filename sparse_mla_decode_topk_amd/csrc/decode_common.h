@@ -40,6 +40,18 @@ __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Range exponent of a block of q values with largest magnitude amax: the largest e with
+// amax * 2^e <= 448 (the e4m3 maximum), clamped to [-100, 100]; 0 for an all-zero block.
+__device__ __forceinline__ int range_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = (int)floorf(__log2f(448.0f / amax));
+  if (ldexpf(amax, e) > 448.0f) --e;
+  return max(-100, min(100, e));
+}
+
+// 2^e as a float for |e| <= 126 (exact).
+__device__ __forceinline__ float exp2_int(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also orders global memory, which
 // makes every wave drain its in-flight HBM -> LDS copies at each barrier; the copies are
 // instead waited for explicitly by the waves that issued them.
@@ -73,10 +85,11 @@ struct Block {
   int row, hb, split, h_lo, nh, total, ntiles;
 };
 
-// Work item of this workgroup: (row, head block, split), or false past the last one.
+// Work item of this workgroup: (row, head block of HB heads, split), or false past the last one.
 // Consecutive blocks are dispatched round-robin over the 8 XCDs; every XCD gets a contiguous
-// range of work items, so the head blocks and splits of a row run side by side on one XCD
-// and share its L2.
+// range of work items, so the head blocks and splits of a row, and neighbouring rows (the MTP
+// rows of a request share records), run side by side on one XCD and share its L2.
+template <int HB = kHB>
 __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
   const int per_xcd = (int)((gridDim.x + 7) / 8);
   const int wg = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
@@ -85,8 +98,26 @@ __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
   const int rest = wg / p.splits;
   bk.hb = rest % p.head_blocks;
   bk.row = rest / p.head_blocks;
-  bk.h_lo = bk.hb * kHB;
-  bk.nh = min(kHB, p.H - bk.h_lo);  // a multiple of 16
+  bk.h_lo = bk.hb * HB;
+  bk.nh = min(HB, p.H - bk.h_lo);  // a multiple of 16
+  return true;
+}
+
+// A row the caller marks empty through its valid count (<= 0): the first split of the row
+// writes out = 0 and lse = -inf for the block's heads; neither q nor the slot list is read.
+// Returns true when the workgroup is done.
+template <int NT>
+__device__ __forceinline__ bool skip_marked_empty(const DecodeParams& p, const Block& bk, int tid) {
+  if (p.valid == nullptr || p.valid[bk.row] > 0) return false;
+  if (bk.split != 0) return true;
+  const int per_row = p.out_fp32 ? 4 * kLatent / 16 : 2 * kLatent / 16;  // 16-byte pieces of one head
+  for (int c = tid; c < bk.nh * per_row; c += NT) {
+    const int h = bk.h_lo + c / per_row, col = c % per_row;
+    uint8_t* row = reinterpret_cast<uint8_t*>(p.out) +
+                   ((int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh) * (p.out_fp32 ? 4 : 2);
+    *reinterpret_cast<i32x4*>(row + 16 * col) = i32x4{0, 0, 0, 0};
+  }
+  if (tid < bk.nh) p.lse[(int64_t)bk.row * p.l_st + (int64_t)(bk.h_lo + tid) * p.l_sh] = -INFINITY;
   return true;
 }
 
@@ -239,14 +270,14 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
 
 // The last split of a (row, head block) to arrive merges every split's partial.  First one
 // thread per head turns the splits' (max, sum) into normalised weights in LDS (and writes the
-// head's LSE); then each thread owns 4 dims of every fourth head and, split by split, loads
-// all of its partial rows before accumulating them, so the merge costs one memory round trip
-// per split rather than several per output element.
-template <class SH, int NT = kThreads>
-__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, SH& sh, int tid) {
-  float* wts = reinterpret_cast<float*>(sh.stage);  // [head][split]; the tile buffers are free now
-  if (tid < bk.nh) {
-    const int h = bk.h_lo + tid;
+// head's LSE); then, CH heads at a time, each thread owns 4 dims of every (NT / 128)-th head and,
+// split by split, loads all of its partial rows before accumulating them, so the merge costs
+// one memory round trip per split rather than several per output element.  `wts` needs
+// HB * splits floats of LDS.
+template <class SH, int NT = kThreads, int HB = kHB>
+__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, SH& sh, float* wts, int tid) {
+  for (int hl = tid; hl < bk.nh; hl += NT) {
+    const int h = bk.h_lo + hl;
     const float* ml = p.ws_ml + ((int64_t)bk.row * p.splits * p.H + h) * 2;  // split sp at + sp * H * 2
     float M = -INFINITY;
 #pragma unroll 8
@@ -257,51 +288,57 @@ __device__ __forceinline__ void combine_splits(const DecodeParams& p, const Bloc
       for (int sp = 0; sp < p.splits; ++sp) {
         const float ms = __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2);
         const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
-        wts[tid * p.splits + sp] = w;
+        wts[hl * p.splits + sp] = w;
         L += w * __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2 + 1);
       }
     }
     const bool empty = !(L > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / L;
-    for (int sp = 0; sp < p.splits; ++sp) wts[tid * p.splits + sp] = empty ? 0.0f : wts[tid * p.splits + sp] * inv;
+    for (int sp = 0; sp < p.splits; ++sp) wts[hl * p.splits + sp] = empty ? 0.0f : wts[hl * p.splits + sp] * inv;
     p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
   }
   __syncthreads();
-  constexpr int kPerThread = kHB * (kLatent / 4) / NT;  // (head, 4-dim) items per thread
+  constexpr int kHeadStep = NT / (kLatent / 4);  // heads one pass of the threads covers
+  constexpr int kPerThread = 16;                 // (head, 4-dim) items per thread and chunk
+  constexpr int CH = kHeadStep * kPerThread;     // heads per chunk
+  static_assert(HB % CH == 0 || CH >= HB, "head chunks");
   const int d4 = tid % (kLatent / 4);
-  const int h0 = tid / (kLatent / 4);  // heads h0, h0 + 4, ... (wave-uniform)
-  f32x4 acc[kPerThread];
+  const int h0 = tid / (kLatent / 4);  // heads h0, h0 + kHeadStep, ... of the chunk (wave-uniform)
+#pragma unroll 1
+  for (int hc = 0; hc < HB; hc += CH) {
+    f32x4 acc[kPerThread];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < p.splits; ++sp) {
-    f32x4 part[kPerThread];
+    for (int i = 0; i < kPerThread; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < p.splits; ++sp) {
+      f32x4 part[kPerThread];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int hl = h0 + (NT / (kLatent / 4)) * i;
-      part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (hl < bk.nh && wts[hl * p.splits + sp] != 0.0f) {
-        const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + bk.h_lo + hl;
-        part[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
+      for (int i = 0; i < kPerThread; ++i) {
+        const int hl = hc + h0 + kHeadStep * i;
+        part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (hl < bk.nh && wts[hl * p.splits + sp] != 0.0f) {
+          const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + bk.h_lo + hl;
+          part[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const int hl = hc + h0 + kHeadStep * i;
+        if (hl < bk.nh) acc[i] += wts[hl * p.splits + sp] * part[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int hl = h0 + (NT / (kLatent / 4)) * i;
-      if (hl < bk.nh) acc[i] += wts[hl * p.splits + sp] * part[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int hl = h0 + (NT / (kLatent / 4)) * i;
-    if (hl >= bk.nh) continue;
-    const int h = bk.h_lo + hl;
-    if (p.out_fp32) {
-      float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc[i];
-    } else {
-      __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-      *reinterpret_cast<bf16x4*>(orow + 4 * d4) =
-          bf16x4{(__bf16)acc[i][0], (__bf16)acc[i][1], (__bf16)acc[i][2], (__bf16)acc[i][3]};
+      const int hl = hc + h0 + kHeadStep * i;
+      if (hl >= bk.nh) continue;
+      const int h = bk.h_lo + hl;
+      if (p.out_fp32) {
+        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
+        *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc[i];
+      } else {
+        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
+        *reinterpret_cast<bf16x4*>(orow + 4 * d4) =
+            bf16x4{(__bf16)acc[i][0], (__bf16)acc[i][1], (__bf16)acc[i][2], (__bf16)acc[i][3]};
+      }
     }
   }
 }

@@ -29,12 +29,13 @@ int device_cus() {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split plan for a decode call.  A workgroup covers up to 64 heads of one row (8 waves, two
-// per SIMD) and its LDS footprint allows one workgroup per CU.  Rows are cut into top-k
-// ranges only when (row, head block) pairs cannot cover every CU of the device.
-DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cus) {
+// Split plan for a decode call whose workgroups cover `hpb` heads of a row: the fp8_ds_mla
+// decode takes every head of a row in one workgroup (kRowHeads), the bf16-record decode 64.
+// Either allows one workgroup per CU.  Rows are cut into top-k ranges only when (row, head
+// block) pairs cannot cover every CU of the device.
+DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cus, int hpb) {
   DecodePlan pl{};
-  pl.head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  pl.head_blocks = (H + hpb - 1) / hpb;
   const int min_splits = K > 0 ? (K + kMaxEntriesPerSplit - 1) / kMaxEntriesPerSplit : 1;
   int splits;
   if (num_splits > 0) {
@@ -45,7 +46,7 @@ DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cu
     splits = 1;
     if (wgs > 0 && wgs < slots) {
       const int64_t want = (slots + wgs - 1) / wgs;
-      const int64_t cap = K / 256 > 1 ? K / 256 : 1;  // keep >= 256 entries (4 tiles) per split
+      const int64_t cap = K / 256 > 1 ? K / 256 : 1;  // keep >= 256 entries (8 tiles) per split
       splits = (int)(want < cap ? want : cap);
     }
     if (splits < min_splits) splits = min_splits;
@@ -60,6 +61,13 @@ DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cu
   }
   pl.ws_total = pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_cnt_bytes;
   return pl;
+}
+
+// Workspace that covers a decode call of either record layout for these sizes.
+size_t decode_workspace(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cus) {
+  const size_t a = make_plan(T, H, K, num_splits, cus, kRowHeads).ws_total;
+  const size_t b = make_plan(T, H, K, num_splits, cus, kHeadsPerBlock).ws_total;
+  return a > b ? a : b;
 }
 
 }  // namespace
@@ -86,9 +94,9 @@ int sparse_mla_convert_index(const int32_t* topk_ids, int64_t ids_ld, const int3
                              int32_t interleave, int32_t* slots, int64_t slots_ld, int32_t* valid_count,
                              hipStream_t stream) {
   if (T < 0 || K < 0) return SMLA_ERR_INVALID_ARG;
-  if (block_size < 1 || dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1)
-    return SMLA_ERR_INVALID_ARG;
+  if (block_size < 1 || dcp_size < 1 || dcp_rank < 0 || interleave < 1) return SMLA_ERR_INVALID_ARG;
   if (bt_rows < 1 || bt_width < 1 || bt_ld < bt_width || ids_ld < K || slots_ld < K) return SMLA_ERR_INVALID_ARG;
+  if (dcp_rank >= dcp_size) return SMLA_ERR_UNSUPPORTED;
   if (T == 0) return SMLA_OK;
   if (K > 0 && (!topk_ids || !req_id_per_token || !block_table || !slots)) return SMLA_ERR_INVALID_ARG;
   if (K > 0 && reinterpret_cast<const void*>(slots) == reinterpret_cast<const void*>(topk_ids) && slots_ld != ids_ld)
@@ -119,7 +127,7 @@ int sparse_mla_convert_index(const int32_t* topk_ids, int64_t ids_ld, const int3
 
 size_t sparse_mla_decode_workspace_size(int32_t T, int32_t H, int32_t K, int32_t num_splits) {
   if (T <= 0 || H < 1 || K < 0 || num_splits < 0 || num_splits > kMaxSplits) return 0;
-  return make_plan(T, H, K, num_splits, num_splits > 0 ? 256 : device_cus()).ws_total;
+  return decode_workspace(T, H, K, num_splits, num_splits > 0 ? 256 : device_cus());
 }
 
 }  // extern "C"
@@ -129,10 +137,10 @@ namespace {
 // Validation and launch parameters of a decode call; nothing is launched.  Shared by the
 // top-k decode and the whole-context decode (which builds its slot lists first).
 int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache, int64_t num_slots,
-                   const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H, int32_t K, float softmax_scale,
+                   const int32_t* slots, int64_t slots_ld, const int32_t* valid_count, int32_t T, int32_t H, int32_t K, float softmax_scale,
                    void* out, int32_t out_dtype, int64_t out_stride_t, int64_t out_stride_h, float* lse,
                    int64_t lse_stride_t, int64_t lse_stride_h, int32_t num_splits, void* workspace,
-                   size_t workspace_bytes, DecodeParams& p, DecodePlan& plan) {
+                   size_t workspace_bytes, int hpb, DecodeParams& p, DecodePlan& plan) {
   if (T < 0 || H < 1 || K < 0 || num_slots < 0) return SMLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return SMLA_ERR_INVALID_ARG;
   if (out_dtype != SMLA_BF16 && out_dtype != SMLA_FP32) return SMLA_ERR_INVALID_ARG;
@@ -146,11 +154,11 @@ int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const 
   if (num_slots > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;  // slots are int32
   const int64_t ovec = out_dtype == SMLA_FP32 ? 4 : 8;  // elements per 16 bytes
   if (!aligned(q, 16) || q_stride_t % 8 != 0 || q_stride_h % 8 != 0 || (kv_cache && !aligned(kv_cache, 16)) ||
-      (slots && !aligned(slots, 4)) || !aligned(out, 16) || out_stride_t % ovec != 0 ||
+      (slots && !aligned(slots, 4)) || (valid_count && !aligned(valid_count, 4)) || !aligned(out, 16) || out_stride_t % ovec != 0 ||
       out_stride_h % ovec != 0 || !aligned(lse, 4))
     return SMLA_ERR_MISALIGNED;
   const int cus = num_splits > 0 ? 256 : device_cus();
-  plan = make_plan(T, H, K, num_splits, cus);
+  plan = make_plan(T, H, K, num_splits, cus, hpb);
   if ((int64_t)K > (int64_t)plan.splits * kMaxEntriesPerSplit) return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)T * plan.head_blocks * plan.splits > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
   if (plan.ws_total > 0) {
@@ -165,6 +173,7 @@ int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const 
   p.num_slots = num_slots;
   p.slots = slots;
   p.slots_ld = slots_ld;
+  p.valid = valid_count;
   p.T = T;
   p.H = H;
   p.K = K;
@@ -179,7 +188,7 @@ int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const 
   p.splits = plan.splits;
   p.entries_per_split = plan.entries_per_split;
   p.head_blocks = plan.head_blocks;
-  p.heads_per_block = kHeadsPerBlock;
+  p.heads_per_block = hpb;
   if (plan.ws_total > 0) {
     char* ws = static_cast<char*>(workspace);
     p.ws_cnt = reinterpret_cast<int32_t*>(ws);
@@ -197,29 +206,31 @@ size_t dense_slots_bytes(int64_t T, int64_t K) { return round_up((size_t)T * (si
 extern "C" {
 
 int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
-                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
+                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,
+                      int32_t T, int32_t H,
                       int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
                       int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
                       int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   DecodeParams p;
   DecodePlan plan;
-  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, T, H, K,
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, valid_count, T, H, K,
                                 softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse, lse_stride_t,
-                                lse_stride_h, num_splits, workspace, workspace_bytes, p, plan);
+                                lse_stride_h, num_splits, workspace, workspace_bytes, kRowHeads, p, plan);
   if (st != SMLA_OK || T == 0) return st;
-  return launch_decode(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+  return launch_decode_row(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
 int sparse_mla_decode_bf16(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
-                           int64_t num_slots, const int32_t* slots, int64_t slots_ld, int32_t T, int32_t H,
+                      int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,
+                      int32_t T, int32_t H,
                            int32_t K, float softmax_scale, void* out, int32_t out_dtype, int64_t out_stride_t,
                            int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
                            int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   DecodeParams p;
   DecodePlan plan;
-  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, T, H, K,
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, valid_count, T, H, K,
                                 softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse, lse_stride_t,
-                                lse_stride_h, num_splits, workspace, workspace_bytes, p, plan);
+                                lse_stride_h, num_splits, workspace, workspace_bytes, kHeadsPerBlock, p, plan);
   if (st != SMLA_OK || T == 0) return st;
   return launch_decode_bf16(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
@@ -231,7 +242,7 @@ size_t sparse_mla_dense_decode_workspace_size(int32_t B, int32_t S, int32_t H, i
   const int64_t T = (int64_t)B * S;
   const int64_t K = dense_list_width(max_seq_len, dcp_size, interleave);
   if (K > (int64_t)kMaxSplits * kMaxEntriesPerSplit) return 0;
-  return dense_slots_bytes(T, K) + make_plan((int32_t)T, H, (int32_t)K, 0, device_cus()).ws_total;
+  return dense_slots_bytes(T, K) + make_plan((int32_t)T, H, (int32_t)K, 0, device_cus(), kRowHeads).ws_total;
 }
 
 int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
@@ -242,8 +253,9 @@ int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_
                             int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                             int64_t lse_stride_h, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || S < 1 || H < 1 || max_seq_len < 0 || block_size < 1) return SMLA_ERR_INVALID_ARG;
-  if (dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1) return SMLA_ERR_INVALID_ARG;
+  if (dcp_size < 1 || dcp_rank < 0 || interleave < 1) return SMLA_ERR_INVALID_ARG;
   if (bt_rows < 1 || bt_width < 1 || bt_ld < bt_width) return SMLA_ERR_INVALID_ARG;
+  if (dcp_rank >= dcp_size) return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)dcp_size * interleave > (1 << 30) || (int64_t)B * S > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
   const int64_t T = (int64_t)B * S;
   const int64_t K = dense_list_width(max_seq_len, dcp_size, interleave);
@@ -258,10 +270,10 @@ int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_
   int32_t* slots = static_cast<int32_t*>(workspace);
   DecodeParams p;
   DecodePlan plan;
-  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, K, (int32_t)T, H,
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, K, nullptr, (int32_t)T, H,
                                 (int32_t)K, softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse,
                                 lse_stride_t, lse_stride_h, 0, static_cast<char*>(workspace) + lists,
-                                workspace_bytes - lists, p, plan);
+                                workspace_bytes - lists, kRowHeads, p, plan);
   if (st != SMLA_OK) return st;
   DenseSlotParams d{};
   d.seq_lens = seq_lens;
@@ -278,7 +290,7 @@ int sparse_mla_dense_decode(const void* q, int64_t q_stride_t, int64_t q_stride_
   d.interleave = interleave;
   d.slots = slots;
   if (launch_dense_slots(d, stream) != hipSuccess) return SMLA_ERR_HIP;
-  return launch_decode(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+  return launch_decode_row(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
 int sparse_mla_merge_lse(const void* out_parts, int32_t part_dtype, int64_t p_stride_s, int64_t p_stride_t,
@@ -330,10 +342,9 @@ int sparse_mla_cache_write(const void* latent, int64_t latent_stride, const void
                            uint8_t* kv_cache, int64_t num_slots, int32_t* slot_mapping, hipStream_t stream) {
   if (N < 0 || num_slots < 0 || latent_stride < 0 || rope_stride < 0) return SMLA_ERR_INVALID_ARG;
   if (in_dtype != SMLA_BF16 && in_dtype != SMLA_FP32) return SMLA_ERR_INVALID_ARG;
-  if (block_size < 1 || dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1)
-    return SMLA_ERR_INVALID_ARG;
+  if (block_size < 1 || dcp_size < 1 || dcp_rank < 0 || interleave < 1) return SMLA_ERR_INVALID_ARG;
   if (bt_rows < 1 || bt_width < 1 || bt_ld < bt_width) return SMLA_ERR_INVALID_ARG;
-  if ((int64_t)dcp_size * interleave > (1 << 30)) return SMLA_ERR_UNSUPPORTED;
+  if (dcp_rank >= dcp_size || (int64_t)dcp_size * interleave > (1 << 30)) return SMLA_ERR_UNSUPPORTED;
   if (N == 0) return SMLA_OK;
   if (!latent || !rope || !positions || !req_id || !block_table || (num_slots > 0 && !kv_cache))
     return SMLA_ERR_INVALID_ARG;
@@ -369,8 +380,8 @@ int sparse_mla_cache_write(const void* latent, int64_t latent_stride, const void
 
 int sparse_mla_dcp_local_seq_lens(const int32_t* seq_lens, int32_t R, int32_t dcp_size, int32_t dcp_rank,
                                   int32_t interleave, int32_t* local_seq_lens, hipStream_t stream) {
-  if (R < 0 || dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size || interleave < 1) return SMLA_ERR_INVALID_ARG;
-  if ((int64_t)dcp_size * interleave > (1 << 30)) return SMLA_ERR_UNSUPPORTED;
+  if (R < 0 || dcp_size < 1 || dcp_rank < 0 || interleave < 1) return SMLA_ERR_INVALID_ARG;
+  if (dcp_rank >= dcp_size || (int64_t)dcp_size * interleave > (1 << 30)) return SMLA_ERR_UNSUPPORTED;
   if (R == 0) return SMLA_OK;
   if (!seq_lens || !local_seq_lens) return SMLA_ERR_INVALID_ARG;
   if (!aligned(seq_lens, 4) || !aligned(local_seq_lens, 4)) return SMLA_ERR_MISALIGNED;

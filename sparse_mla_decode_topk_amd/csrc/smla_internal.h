@@ -14,7 +14,8 @@ constexpr int kScaleOffset = 512;
 constexpr int kRopeOffset = 528;
 constexpr int kMaxEntriesPerSplit = 4096;  // slot entries one decode workgroup compacts
 constexpr int kMaxSplits = 64;
-constexpr int kHeadsPerBlock = 64;           // heads one decode workgroup covers
+constexpr int kHeadsPerBlock = 64;           // heads one workgroup of the bf16-record decode covers
+constexpr int kRowHeads = 128;               // heads one workgroup of the fp8_ds_mla decode covers (all)
 
 struct ConvertParams {
   const int32_t* ids;
@@ -37,6 +38,7 @@ struct DecodeParams {
   int64_t num_slots;
   const int32_t* slots;
   int64_t slots_ld;
+  const int32_t* valid;  // [T] optional: a row whose count is <= 0 is empty and its list is not read
   int32_t T, H, K;
   float scale_log2;  // softmax_scale * log2(e)
   void* out;
@@ -98,7 +100,7 @@ struct DecodePlan {
 };
 
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode_row(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);

@@ -24,8 +24,8 @@ from . import _binding as B
 class DcpDecodeStep:
     def __init__(self, *, T: int, H: int, K: int, dcp_size: int, block_size: int, softmax_scale: float,
                  out_dtype: torch.dtype = torch.bfloat16, partial_dtype: torch.dtype = torch.float32,
-                 lse_layout: str = "HT", device="cuda", num_splits: int = 0):
-        self.T, self.H, self.K, self.D = T, H, K, dcp_size
+                 lse_layout: str = "HT", device="cuda", num_splits: int = 0, interleave: int = 1):
+        self.T, self.H, self.K, self.D, self.interleave = T, H, K, dcp_size, interleave
         self.block_size, self.scale, self.num_splits = block_size, float(softmax_scale), num_splits
         dev = torch.device(device)
         self.slots = torch.empty((dcp_size, T, K), dtype=torch.int32, device=dev)
@@ -55,17 +55,17 @@ class DcpDecodeStep:
             raise ValueError("one (cache, block table) pair per shard")
         stream = torch.cuda.current_stream(q.device)
         for r, (cache, bt) in enumerate(shards):
-            B.convert_index(ids, req, bt, self.block_size, dcp_size=self.D, dcp_rank=r, interleave=1,
-                            out=self.slots[r], with_valid_count=False)
+            sl, vc = B.convert_index(ids, req, bt, self.block_size, dcp_size=self.D, dcp_rank=r,
+                                     interleave=self.interleave, out=self.slots[r], valid=self.valid[r])
             if decode_events is not None:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record(stream)
             if self.D == 1:
                 B.decode(q, cache, self.slots[r], self.scale, out=self.out, lse=self.lse, num_splits=self.num_splits,
-                         workspace=self.workspace)
+                         workspace=self.workspace, valid_count=vc)
             else:
                 B.decode(q, cache, self.slots[r], self.scale, out=self.parts[r], lse=self.lse_parts[r],
-                         num_splits=self.num_splits, workspace=self.workspace)
+                         num_splits=self.num_splits, workspace=self.workspace, valid_count=vc)
             if decode_events is not None:
                 ev[1].record(stream)
                 decode_events.append(ev)

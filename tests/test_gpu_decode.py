@@ -211,3 +211,65 @@ def test_decode_longest_list():
     out, lse = gpu_decode(w, out_dtype=torch.float32)
     ref_o, ref_l = oracle_unsharded(w)
     check_close(out, lse, ref_o, ref_l, what="K262144")
+
+
+def _wide_range_q(w, seed):
+    """q whose values inside each head span a wide range: one or two dims per (row, head) at
+    +-2^5 .. 2^7 and every other dim +-2^u with u uniform in [-14, -2], all exact in bf16.  Small
+    values next to a large one are where a split of q into two e4m3 terms under one range factor
+    per head stops being exact."""
+    import dataclasses
+
+    rng = np.random.default_rng(seed)
+    T, H = w.T, w.H
+    mag = np.exp2(rng.uniform(-14.0, -2.0, size=(T, H, 576)))
+    q = (mag * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float32)
+    for t in range(T):
+        for h in range(H):
+            for d in rng.choice(576, size=int(rng.integers(1, 3)), replace=False):
+                q[t, h, d] = np.float32(rng.choice([-1.0, 1.0]) * np.exp2(rng.uniform(5.0, 7.0)))
+    bits = torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return dataclasses.replace(w, q_bits=bits)
+
+
+@pytest.mark.parametrize("kv", ["fp8_ds_mla", "bf16"])
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_query_range_within_head(kv, H, splits):
+    w = _wide_range_q(make_random(131 + H, T=6, H=H, K=400, ctx=900, B=64, neg_frac=0.1, n_req=2, kv=kv), 7 + H)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    print(f"decode wide-range q kv={kv} H={H} splits={splits}", flush=True)
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32,
+                           num_splits=splits, kv_layout=kv)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale, record_layout=kv)
+    do, dl = check_close(out, lse, ref_o, ref_l, what=f"wide-range q {kv} H{H} s{splits}")
+    print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("kv", ["fp8_ds_mla", "bf16"])
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_valid_count_matches_slots(kv, H, splits):
+    """Counts from the conversion change nothing but skip the rows they mark empty: with and without
+    them the results are bitwise equal; a row counted 0 is (0, -inf) even if its slots hold entries."""
+    w = make_random(141 + H, T=9, H=H, K=300, ctx=700, B=64, neg_frac=0.2, n_req=3, kv=kv)
+    w.ids[2, :] = -1
+    w.ids[5, :] = -1
+    slots, counts = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    cache = w.cache.to_device("cuda")
+    ds = dev(slots)
+    a = smla.decode(q_dev(w), cache, ds, w.sm_scale, out_dtype=torch.float32, num_splits=splits, kv_layout=kv)
+    b = smla.decode(q_dev(w), cache, ds, w.sm_scale, out_dtype=torch.float32, num_splits=splits, kv_layout=kv,
+                    valid_count=dev(counts.astype(np.int32)))
+    torch.cuda.synchronize()
+    assert counts[2] == 0 and counts[5] == 0
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    forced = counts.astype(np.int32).copy()
+    forced[7] = 0  # a row the caller marks empty: its slots are not read
+    o, l = smla.decode(q_dev(w), cache, ds, w.sm_scale, out_dtype=torch.bfloat16, num_splits=splits, kv_layout=kv,
+                       valid_count=dev(forced))
+    torch.cuda.synchronize()
+    assert torch.all(o[7] == 0) and torch.all(torch.isneginf(l[7]))
+    keep = [t for t in range(w.T) if t != 7]
+    assert torch.equal(l[keep], a[1][keep])

@@ -60,21 +60,33 @@ def test_dcp4_c2_full():
                 what="c2 merged vs unsharded gpu")
 
 
-def test_dcp2_c3_full_size_sampled():
-    """The timed configuration: MTP rows, H=128, top-k 2048, DCP2, kernel-native (H,T) LSE."""
+def test_dcp2_c3_full_size_every_row():
+    """The timed configuration: MTP rows, H=128, top-k 2048, DCP2, kernel-native (H,T) LSE; every
+    row of the merged step and of the unsharded decode against the oracle."""
     w = make_config(3)
     print(f"c3: T={w.T} H={w.H} K={w.K}", flush=True)
     step, out, lse = run_step(w, lse_layout="HT")
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
-    rows = list(range(0, w.T, 17)) + [w.T - 1]
-    ref_o, ref_l = oracle_unsharded(w, rows)
-    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, what="c3 sampled rows")
-    print(f"  sampled rows max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+    ref_o, ref_l = oracle_unsharded(w)
+    do, dl = check_close(out, lse, ref_o, ref_l, what="c3 merged, every row")
+    print(f"  merged max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
     uo, ul = unsharded_gpu(w)
-    check_close(out, lse, uo.float().cpu().numpy().astype(np.float64), ul.cpu().numpy().astype(np.float64),
-                what="c3 merged vs unsharded gpu")
-    ref_o, ref_l = oracle_unsharded(w, rows)
-    check_close(uo[rows], ul[rows], ref_o, ref_l, what="c3 unsharded sampled rows")
+    do, dl = check_close(uo, ul, ref_o, ref_l, what="c3 unsharded, every row")
+    print(f"  unsharded max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+
+
+def test_dcp4_c2_counts_change_nothing():
+    """The step passes the conversion's counts to every shard decode; without them the partials are
+    bitwise the same (shards 2 and 3 count 0 for the four context-2 rows)."""
+    w = make_config(2)
+    shards = device_shards(w)
+    step, out, lse = run_step(w, shards=shards)
+    vc = step.valid.cpu().numpy()
+    assert np.all(vc[2:, 32:] == 0) and np.all(vc[:2, 32:] == 1)
+    for r, (cache, bt) in enumerate(shards):
+        o, l = smla.decode(q_dev(w), cache, step.slots[r], w.sm_scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o, step.parts[r]) and torch.equal(l, step.lse_parts[r])
 
 
 def test_dcp8_c4_subset_rows_full_caches():
@@ -87,21 +99,23 @@ def test_dcp8_c4_subset_rows_full_caches():
     print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
 
 
-def test_dcp8_c4_full_size_sampled():
-    """The mixed batch at its full size (T = 4224, 8 shards), in the launch the c4 bench line times;
-    sampled rows against the oracle: decode rows, and prefill rows at positions 0-9 (a row at position
-    p has p + 1 candidates, so up to 7 of its 8 shards own none and must drop out of the merge) and
-    further along both prompts."""
+def test_dcp8_c4_full_size_rows():
+    """The mixed batch at its full size (T = 4224, 8 shards), in the launch the c4 bench line times,
+    against the oracle on every decode row, every prefill row at positions 0-63 (a row at position p
+    has p + 1 candidates, so up to 7 of its 8 shards own none and must drop out of the merge) and a
+    sample further along both prompts."""
     w = make_config(4)
     print(f"c4 full: T={w.T} H={w.H} D={w.dcp_size}", flush=True)
     step, out, lse = run_step(w, lse_layout="HT")
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
     pos = np.asarray(w.row_pos)
-    short = [int(r) for r in np.flatnonzero(pos < 10)]
-    rows = sorted(set(range(0, w.T, 101)) | set(short) | {w.T - 1})
+    decode_rows = [int(r) for r in np.flatnonzero(pos == pos.max())]
+    short = [int(r) for r in np.flatnonzero(pos < 64)]
+    assert len(decode_rows) == 128 and len(short) == 128
+    rows = sorted(set(decode_rows) | set(short) | set(range(0, w.T, 37)) | {w.T - 1})
     ref_o, ref_l = oracle_unsharded(w, rows)
-    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, what="c4 sampled rows")
-    print(f"  {len(rows)} sampled rows max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, what="c4 rows")
+    print(f"  {len(rows)} rows max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("S,dtype", [(1, torch.float32), (2, torch.float32), (4, torch.bfloat16), (8, torch.float32)])

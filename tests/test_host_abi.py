@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smla_abi_version() == 2
+    assert lib.smla_abi_version() == 3
     for st in range(0, 7):
         assert isinstance(lib.smla_status_string(st), bytes) and lib.smla_status_string(st)
 
@@ -63,7 +63,7 @@ def convert_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(T=-1), INVALID), (dict(K=-1), INVALID), (dict(B=0), INVALID), (dict(D=0), INVALID),
-    (dict(D=2, r=2), INVALID), (dict(r=-1), INVALID), (dict(I=0), INVALID), (dict(ids_ld=4), INVALID),
+    (dict(D=2, r=2), UNSUPPORTED), (dict(r=-1), INVALID), (dict(I=0), INVALID), (dict(ids_ld=4), INVALID),
     (dict(out_ld=4), INVALID), (dict(bt_ld=2), INVALID), (dict(bt_rows=0), INVALID), (dict(ids=None), INVALID),
     (dict(out=None), INVALID), (dict(req=None), INVALID), (dict(bt=None), INVALID),
     (dict(ids=A16 + 2), MISALIGNED), (dict(valid=A16 + 1), MISALIGNED),
@@ -81,12 +81,12 @@ def test_convert_accepts_4_byte_aligned_index_arrays(lib):
 
 
 def decode_call(lib, **kw):
-    a = dict(q=A16, qst=128 * 576, qsh=576, kv=A16, ns=100, slots=A16, sld=64, T=2, H=128, K=64, scale=0.07,
-             out=A16, odt=0, ost=128 * 512, osh=512, lse=A16, lst=128, lsh=1, splits=0, ws=None, wsb=0)
+    a = dict(q=A16, qst=128 * 576, qsh=576, kv=A16, ns=100, slots=A16, sld=64, valid=None, T=2, H=128, K=64,
+             scale=0.07, out=A16, odt=0, ost=128 * 512, osh=512, lse=A16, lst=128, lsh=1, splits=0, ws=None, wsb=0)
     a.update(kw)
-    return lib.sparse_mla_decode(a["q"], a["qst"], a["qsh"], a["kv"], a["ns"], a["slots"], a["sld"], a["T"], a["H"],
-                                 a["K"], a["scale"], a["out"], a["odt"], a["ost"], a["osh"], a["lse"], a["lst"],
-                                 a["lsh"], a["splits"], a["ws"], a["wsb"], None)
+    return lib.sparse_mla_decode(a["q"], a["qst"], a["qsh"], a["kv"], a["ns"], a["slots"], a["sld"], a["valid"],
+                                 a["T"], a["H"], a["K"], a["scale"], a["out"], a["odt"], a["ost"], a["osh"], a["lse"],
+                                 a["lst"], a["lsh"], a["splits"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -99,18 +99,18 @@ def decode_call(lib, **kw):
     (dict(kv=A16 + 8), MISALIGNED), (dict(slots=A16 + 2), MISALIGNED), (dict(out=A16 + 8), MISALIGNED),
     (dict(odt=1, osh=514), MISALIGNED), (dict(lse=A16 + 2), MISALIGNED),
     (dict(K=8192, sld=8192, splits=1), UNSUPPORTED), (dict(K=128, sld=128, splits=2), WORKSPACE),
-    (dict(K=128, sld=128, splits=2, ws=A16 + 64, wsb=1 << 30), MISALIGNED),
+    (dict(K=128, sld=128, splits=2, ws=A16 + 64, wsb=1 << 30), MISALIGNED), (dict(valid=A16 + 2), MISALIGNED),
     (dict(T=0), OK), (dict(T=0, q=None, out=None), OK),
 ])
 def test_decode_validation(lib, kw, want):
     assert decode_call(lib, **kw) == want
     # the bf16-record decode validates its arguments the same way
-    a = dict(q=A16, qst=128 * 576, qsh=576, kv=A16, ns=100, slots=A16, sld=64, T=2, H=128, K=64, scale=0.07,
-             out=A16, odt=0, ost=128 * 512, osh=512, lse=A16, lst=128, lsh=1, splits=0, ws=None, wsb=0)
+    a = dict(q=A16, qst=128 * 576, qsh=576, kv=A16, ns=100, slots=A16, sld=64, valid=None, T=2, H=128, K=64,
+             scale=0.07, out=A16, odt=0, ost=128 * 512, osh=512, lse=A16, lst=128, lsh=1, splits=0, ws=None, wsb=0)
     a.update(kw)
-    assert lib.sparse_mla_decode_bf16(a["q"], a["qst"], a["qsh"], a["kv"], a["ns"], a["slots"], a["sld"], a["T"],
-                                      a["H"], a["K"], a["scale"], a["out"], a["odt"], a["ost"], a["osh"], a["lse"],
-                                      a["lst"], a["lsh"], a["splits"], a["ws"], a["wsb"], None) == want
+    assert lib.sparse_mla_decode_bf16(a["q"], a["qst"], a["qsh"], a["kv"], a["ns"], a["slots"], a["sld"], a["valid"],
+                                      a["T"], a["H"], a["K"], a["scale"], a["out"], a["odt"], a["ost"], a["osh"],
+                                      a["lse"], a["lst"], a["lsh"], a["splits"], a["ws"], a["wsb"], None) == want
 
 
 def test_workspace_size(lib):
@@ -155,7 +155,7 @@ def cache_write_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(N=-1), INVALID), (dict(ns=-1), INVALID), (dict(dt=2), INVALID), (dict(B=0), INVALID), (dict(D=0), INVALID),
-    (dict(D=2, r=2), INVALID), (dict(I=0), INVALID), (dict(bt_ld=2), INVALID), (dict(bt_rows=0), INVALID),
+    (dict(D=2, r=2), UNSUPPORTED), (dict(r=-1), INVALID), (dict(I=0), INVALID), (dict(bt_ld=2), INVALID), (dict(bt_rows=0), INVALID),
     (dict(lst=256), INVALID), (dict(rst=32), INVALID), (dict(lat=None), INVALID), (dict(rope=None), INVALID),
     (dict(pos=None), INVALID), (dict(req=None), INVALID), (dict(bt=None), INVALID), (dict(kv=None), INVALID),
     (dict(D=1 << 16, I=1 << 15), UNSUPPORTED),
@@ -169,7 +169,8 @@ def test_cache_write_validation(lib, kw, want):
 
 
 @pytest.mark.parametrize("args,want", [
-    ((A16, -1, 1, 0, 1, A16), INVALID), ((A16, 4, 0, 0, 1, A16), INVALID), ((A16, 4, 2, 2, 1, A16), INVALID),
+    ((A16, -1, 1, 0, 1, A16), INVALID), ((A16, 4, 0, 0, 1, A16), INVALID), ((A16, 4, 2, 2, 1, A16), UNSUPPORTED),
+    ((A16, 4, 2, -1, 1, A16), INVALID),
     ((A16, 4, 2, 0, 0, A16), INVALID), ((None, 4, 2, 0, 1, A16), INVALID), ((A16, 4, 2, 0, 1, None), INVALID),
     ((A16 + 2, 4, 2, 0, 1, A16), MISALIGNED), ((A16, 4, 2, 0, 1, A16 + 1), MISALIGNED),
     ((None, 0, 2, 1, 1, None), OK),
@@ -191,7 +192,8 @@ def dense_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(B=-1), INVALID), (dict(S=0), INVALID), (dict(H=0), INVALID), (dict(maxlen=-1), INVALID),
-    (dict(blk=0), INVALID), (dict(D=2, r=2), INVALID), (dict(I=0), INVALID), (dict(bt_ld=4), INVALID),
+    (dict(blk=0), INVALID), (dict(D=2, r=2), UNSUPPORTED), (dict(r=-1), INVALID), (dict(I=0), INVALID),
+    (dict(bt_ld=4), INVALID),
     (dict(bt_rows=0), INVALID), (dict(sl=None), INVALID), (dict(bt=None), INVALID), (dict(q=None), INVALID),
     (dict(scale=0.0), INVALID), (dict(H=40), UNSUPPORTED), (dict(maxlen=(1 << 18) + 1), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=A16 * 16 + 16), MISALIGNED),
