@@ -1,4 +1,5 @@
-"""Build libsmla.so (HIP, gfx950) in-tree with hipcc.
+"""Build libsmla.so (HIP, gfx950) in-tree with hipcc, and libsmla_peak.so (the achievable-peak
+microbenchmarks of csrc/peak.hip, measurement only).
 
     python -m sparse_mla_decode_topk_amd.build
 
@@ -20,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsmla.so")
+PEAK_LIB = os.path.join(PKG, "libsmla_peak.so")
 SOURCES = ["smla_api.hip", "convert_index.hip", "decode_row.hip", "merge_lse.hip", "cache_write.hip", "dense_slots.hip",
            "decode_bf16.hip"]
 EXTRA_FLAGS = {"decode_row.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
@@ -44,7 +46,7 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link LIB; returns its path."""
+    """Compile every HIP source and link LIB and PEAK_LIB; returns LIB's path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="smla_build_") as tmp:
         def compile_one(src):
@@ -53,13 +55,14 @@ def build(verbose: bool = False) -> str:
                   "-c", os.path.join(CSRC, src), "-o", obj])
             return obj
 
-        with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-            objs = list(ex.map(compile_one, SOURCES))
-        out = LIB + ".tmp"
-        log = _run([cc, f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", out, *objs])
-        if verbose:
-            sys.stdout.write(log)
-        os.replace(out, LIB)
+        with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+            objs = list(ex.map(compile_one, SOURCES + ["peak.hip"]))
+        for lib, group in ((LIB, objs[:-1]), (PEAK_LIB, objs[-1:])):
+            out = lib + ".tmp"
+            log = _run([cc, f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", out, *group])
+            if verbose:
+                sys.stdout.write(log)
+            os.replace(out, lib)
     return LIB
 
 

@@ -225,24 +225,33 @@ __device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& b
   }
 }
 
-// Compacts this split's slot entries that lie in [0, num_slots) into sh.clist, in order;
-// returns their number.  No front-pack is needed upstream.
+// Compacts this split's slot entries that lie in [0, num_slots) into sh.clist, in a fixed
+// order (attention sums over the set); returns their number.  No front-pack is needed upstream.  Every thread loads all of its
+// entries first (at most kMaxEntriesPerSplit / NT), so the list costs one memory round trip;
+// then groups of 4 * NT entries are placed in order, two barriers per group.
 template <class SH, int NT = kThreads>
 __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block& bk, SH& sh, int tid, int wave,
                                              int lane) {
+  constexpr int kPer = kMaxEntriesPerSplit / NT;
+  static_assert(kPer % 4 == 0, "entries per thread come in groups of four");
   const int e0 = bk.split * p.entries_per_split;
   const int e1 = min(p.K, e0 + p.entries_per_split);
   const int32_t* srow = p.slots + (int64_t)bk.row * p.slots_ld;
+  int vals[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = e0 + i * NT + tid;
+    vals[i] = e < e1 ? srow[e] : -1;
+  }
   int total = 0;
-  for (int base = e0; base < e1; base += NT * 4) {
-    int vals[4];
+#pragma unroll
+  for (int grp = 0; grp < kPer / 4; ++grp) {
+    if (e0 + grp * 4 * NT >= e1) break;  // uniform across the workgroup
     int wcount = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = base + i * NT + tid;
-      const int v = e < e1 ? srow[e] : -1;
-      const bool ok = v >= 0 && (int64_t)v < p.num_slots;
-      vals[i] = ok ? v : -1;
+    for (int i = 4 * grp; i < 4 * grp + 4; ++i) {
+      const bool ok = vals[i] >= 0 && (int64_t)vals[i] < p.num_slots;
+      vals[i] = ok ? vals[i] : -1;
       wcount += __popcll(__ballot(ok));
     }
     if (lane == 0) sh.wave_cnt[wave] = wcount;
@@ -256,7 +265,7 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
     }
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 4 * grp; i < 4 * grp + 4; ++i) {
       const bool ok = vals[i] >= 0;
       const unsigned long long bm = __ballot(ok);
       if (ok) sh.clist[off + __popcll(bm & below)] = vals[i];

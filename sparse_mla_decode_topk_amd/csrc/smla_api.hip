@@ -29,9 +29,9 @@ int device_cus() {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split plan for a decode call whose workgroups cover `hpb` heads of a row: the fp8_ds_mla
-// decode takes every head of a row in one workgroup (kRowHeads), the bf16-record decode 64.
-// Either allows one workgroup per CU.  Rows are cut into top-k ranges only when (row, head
+// Split plan for a decode call whose workgroups cover `hpb` heads of a row (kRowHeads for the
+// fp8_ds_mla decode, kHeadsPerBlock for the bf16-record decode).  Either allows one workgroup
+// per CU.  Rows are cut into top-k ranges only when (row, head
 // block) pairs cannot cover every CU of the device.
 DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cus, int hpb) {
   DecodePlan pl{};

@@ -15,7 +15,7 @@ constexpr int kRopeOffset = 528;
 constexpr int kMaxEntriesPerSplit = 4096;  // slot entries one decode workgroup compacts
 constexpr int kMaxSplits = 64;
 constexpr int kHeadsPerBlock = 64;           // heads one workgroup of the bf16-record decode covers
-constexpr int kRowHeads = 128;               // heads one workgroup of the fp8_ds_mla decode covers (all)
+constexpr int kRowHeads = 64;                // heads one workgroup of the fp8_ds_mla decode covers
 
 struct ConvertParams {
   const int32_t* ids;
