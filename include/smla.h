@@ -47,6 +47,9 @@ extern "C" {
 
 #define SMLA_ABI_VERSION 3
 
+/* Bytes of the per-device scratch array behind sparse_mla_decode_noalloc (32 MiB). */
+#define SMLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
 enum smla_status {
   SMLA_OK = 0,
   SMLA_ERR_INVALID_ARG = 1, /* null required pointer, negative size or stride        */
@@ -156,6 +159,27 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
                       int64_t out_stride_t,
                       int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
                       int32_t num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sparse_mla_decode_noalloc - sparse_mla_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The call allocates nothing and calls no allocating routine; its split
+ * partials and arrival counters live in a scratch array the library holds on each device it runs
+ * on (SMLA_NOALLOC_SCRATCH_BYTES, kept until the process ends).
+ *
+ * Arguments, layouts, results and errors are those of sparse_mla_decode (same kernels, same
+ * split plan), except: the workspace is the library's scratch array; a call whose split plan
+ * needs more than SMLA_NOALLOC_SCRATCH_BYTES (see sparse_mla_decode_workspace_size) returns
+ * SMLA_ERR_WORKSPACE and launches nothing; SMLA_ERR_HIP if the runtime cannot give the scratch
+ * array's device address.  Every call on one device shares that device's array, and each call
+ * clears the counters it needs, so calls on one device must not overlap in time (calls on
+ * different streams of one device race).
+ */
+int sparse_mla_decode_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                              int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,
+                              int32_t T, int32_t H, int32_t K, float softmax_scale, void* out, int32_t out_dtype,
+                              int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                              int64_t lse_stride_h, int32_t num_splits, hipStream_t stream);
 
 /*
  * sparse_mla_decode_bf16 - sparse_mla_decode over a plain bf16 latent cache instead of the

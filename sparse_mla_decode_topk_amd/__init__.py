@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     convert_index,
     dcp_local_seq_lens,
     decode,
+    decode_noalloc,
     decode_workspace_size,
     dense_decode,
     lib_path,
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     sparse_mla_dcp_local_seq_lens,
     sparse_mla_decode,
     sparse_mla_decode_bf16,
+    sparse_mla_decode_noalloc,
     sparse_mla_decode_workspace_size,
     sparse_mla_dense_decode,
     sparse_mla_dense_decode_workspace_size,

@@ -64,6 +64,9 @@ def load_library():
                                           _I64, _I64, _P, _I64, _I64, _I32, _P, _SZ, _P]
         lib.sparse_mla_decode_bf16.restype = ctypes.c_int
         lib.sparse_mla_decode_bf16.argtypes = lib.sparse_mla_decode.argtypes
+        lib.sparse_mla_decode_noalloc.restype = ctypes.c_int
+        lib.sparse_mla_decode_noalloc.argtypes = [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _P,
+                                                  _I32, _I64, _I64, _P, _I64, _I64, _I32, _P]
         lib.sparse_mla_merge_lse.restype = ctypes.c_int
         lib.sparse_mla_merge_lse.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I32,
                                              _I64, _I64, _P, _I64, _I64, _P]
@@ -142,6 +145,10 @@ def sparse_mla_decode(*args) -> int:
 
 def sparse_mla_decode_bf16(*args) -> int:
     return load_library().sparse_mla_decode_bf16(*args)
+
+
+def sparse_mla_decode_noalloc(*args) -> int:
+    return load_library().sparse_mla_decode_noalloc(*args)
 
 
 def sparse_mla_merge_lse(*args) -> int:
@@ -227,6 +234,42 @@ def convert_index(topk_ids: torch.Tensor, req_id_per_token: torch.Tensor, block_
 
 
 KV_LAYOUTS = {"fp8_ds_mla": RECORD_BYTES, "bf16": 2 * HEAD_DIM}
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax_scale: float,
+                   out: torch.Tensor, lse: torch.Tensor, num_splits: int = 0,
+                   valid_count: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """sparse_mla_decode_noalloc: the fp8_ds_mla decode with the library's per-device scratch array
+    as workspace.  The caller passes out [T,H,512] (bf16 or fp32) and lse viewable as [T,H]; nothing
+    is allocated here or in the library.  Calls on one device must not overlap."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_cache, "kv_cache", torch.uint8, 2)
+    _need(slots, "slots", torch.int32, 2)
+    T, H, D = q.shape
+    if D != HEAD_DIM or q.stride(2) != 1:
+        raise ValueError("q must be [T,H,576] with contiguous dims")
+    if kv_cache.shape[1] != RECORD_BYTES or not kv_cache.is_contiguous():
+        raise ValueError(f"kv_cache must be a contiguous [num_slots,{RECORD_BYTES}] uint8 tensor")
+    K = slots.shape[1]
+    if slots.shape[0] != T or (K > 1 and slots.stride(1) != 1):
+        raise ValueError("slots must be [T,K] with a contiguous last dimension")
+    if valid_count is not None:
+        _need(valid_count, "valid_count", torch.int32, 1)
+        if valid_count.shape[0] != T or (T > 1 and valid_count.stride(0) != 1):
+            raise ValueError("valid_count must be a contiguous [T] int32 tensor")
+    _need(out, "out", out.dtype, 3)
+    if tuple(out.shape) != (T, H, LATENT_DIM) or out.stride(2) != 1:
+        raise ValueError("out must be [T,H,512] with contiguous dims")
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(lse.shape) != (T, H):
+        raise ValueError("lse must be viewable as [T,H]")
+    st = sparse_mla_decode_noalloc(
+        q.data_ptr(), _st(q, 0), _st(q, 1), kv_cache.data_ptr(), kv_cache.shape[0], slots.data_ptr(),
+        _st(slots, 0), valid_count.data_ptr() if valid_count is not None else None, T, H, K, float(softmax_scale),
+        out.data_ptr(), _dtype_code(out.dtype), _st(out, 0), _st(out, 1), lse.data_ptr(), _st(lse, 0), _st(lse, 1),
+        num_splits, _stream(q.device))
+    _check("sparse_mla_decode_noalloc", st)
+    return out, lse
 
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, slots: torch.Tensor, softmax_scale: float,

@@ -201,6 +201,23 @@ int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const 
 // Bytes of the slot lists a whole-context decode keeps at the front of its workspace.
 size_t dense_slots_bytes(int64_t T, int64_t K) { return round_up((size_t)T * (size_t)K * sizeof(int32_t), 256); }
 
+// Workspace of sparse_mla_decode_noalloc: one copy per device, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not the device memory: the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, or null if the runtime cannot give it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  g_scratch[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,6 +233,22 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
   const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, valid_count, T, H, K,
                                 softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse, lse_stride_t,
                                 lse_stride_h, num_splits, workspace, workspace_bytes, kRowHeads, p, plan);
+  if (st != SMLA_OK || T == 0) return st;
+  return launch_decode_row(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+int sparse_mla_decode_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
+                              int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,
+                              int32_t T, int32_t H, int32_t K, float softmax_scale, void* out, int32_t out_dtype,
+                              int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                              int64_t lse_stride_h, int32_t num_splits, hipStream_t stream) {
+  void* ws = scratch_address();
+  if (!ws) return SMLA_ERR_HIP;
+  DecodeParams p;
+  DecodePlan plan;
+  const int st = prepare_decode(q, q_stride_t, q_stride_h, kv_cache, num_slots, slots, slots_ld, valid_count, T, H, K,
+                                softmax_scale, out, out_dtype, out_stride_t, out_stride_h, lse, lse_stride_t,
+                                lse_stride_h, num_splits, ws, SMLA_NOALLOC_SCRATCH_BYTES, kRowHeads, p, plan);
   if (st != SMLA_OK || T == 0) return st;
   return launch_decode_row(p, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
