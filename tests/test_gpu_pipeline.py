@@ -89,6 +89,24 @@ def test_dcp4_c2_counts_change_nothing():
         assert torch.equal(o, step.parts[r]) and torch.equal(l, step.lse_parts[r])
 
 
+@pytest.mark.parametrize("D,I,H,splits", [(2, 2, 128, 0), (2, 3, 64, 3), (4, 2, 64, 0), (4, 3, 128, 2)])
+def test_interleaved_dcp_pipeline(D, I, H, splits):
+    """DCP with interleave I (page "FlashMLA sparse fp8 path gains DCP and MTP", Implementation
+    breakdown step 4): rank r holds the tokens p with (p // I) % D == r; the merged step equals the
+    unsharded oracle."""
+    w = make_random(500 + 10 * D + I, T=10, H=H, K=320, ctx=1200, B=64, D=D, neg_frac=0.15, n_req=3, interleave=I)
+    print(f"D={D} I={I} H={H} splits={splits}", flush=True)
+    step, out, lse = run_step(w, interleave=I, num_splits=splits)
+    ref_o, ref_l = oracle_unsharded(w)
+    do, dl = check_close(out, lse, ref_o, ref_l, what=f"D{D} I{I}")
+    print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
+    counts = step.valid.cpu().numpy()  # per shard and row: the ids each rank owns
+    ids = np.asarray(w.ids)
+    for r in range(D):
+        own = (ids >= 0) & ((ids // I) % D == r)
+        assert np.array_equal(counts[r], own.sum(axis=1))
+
+
 def test_dcp8_c4_subset_rows_full_caches():
     """Mixed batch at full context (131072-token decode requests, 8 shards) on a row subset."""
     w = make_config(4, scale_rows=48)

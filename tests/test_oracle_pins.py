@@ -147,14 +147,14 @@ def check_convert_hand(convert=O.convert_index):
 
 
 def check_convert_partition(w, convert=O.convert_index):
-    """Every valid id lands on exactly one shard; the shard record is the id's record;
-    local position * D + rank recovers the id."""
-    D = w.dcp_size
+    """Every valid id lands on exactly one shard; the shard record is the id's record; the
+    local position L recovers the id: (L // I) * I * D + rank * I + L % I (L * D + rank at I = 1)."""
+    D, I = w.dcp_size, w.interleave
     g_slots, g_valid = convert(w.ids, w.req, w.block_table, w.block_size)
     owners = np.zeros(w.ids.shape, dtype=np.int64)
     total = np.zeros(w.T, dtype=np.int64)
     for sh in w.shards:
-        s, v = convert(w.ids, w.req, sh.block_table, w.block_size, dcp_size=D, dcp_rank=sh.rank)
+        s, v = convert(w.ids, w.req, sh.block_table, w.block_size, dcp_size=D, dcp_rank=sh.rank, interleave=I)
         ok = s >= 0
         owners += ok
         total += v
@@ -167,7 +167,8 @@ def check_convert_partition(w, convert=O.convert_index):
         blk, off = slot // w.block_size, slot % w.block_size
         for t, j, b_, o_ in zip(rows[:512], cols[:512], blk[:512], off[:512]):
             lb = int(np.nonzero(sh.block_table[w.req[t]] == b_)[0][0])
-            assert (lb * w.block_size + o_) * D + sh.rank == w.ids[t, j]
+            L = lb * w.block_size + o_
+            assert (L // I) * I * D + sh.rank * I + L % I == w.ids[t, j]
     valid_in = (w.ids >= 0)
     assert np.array_equal(owners, valid_in.astype(np.int64))
     assert np.array_equal(total, g_valid)
@@ -229,7 +230,8 @@ def check_merge_shards(w, rows, merge=O.merge_lse, convert=O.convert_index, atte
     q = sub.q_f32()
     parts_o, parts_l = [], []
     for sh in sub.shards:
-        s, _ = convert(sub.ids, sub.req, sh.block_table, sub.block_size, dcp_size=sub.dcp_size, dcp_rank=sh.rank)
+        s, _ = convert(sub.ids, sub.req, sh.block_table, sub.block_size, dcp_size=sub.dcp_size, dcp_rank=sh.rank,
+                       interleave=sub.interleave)
         o, l = attention(q, s, sh.cache, sh.cache.num_slots, sub.sm_scale)
         parts_o.append(o)
         parts_l.append(l)
@@ -365,6 +367,20 @@ def test_closed_forms():
 @pytest.mark.parametrize("D", [2, 4, 8])
 def test_merge_of_shards_equals_unsharded(D):
     w = make_random(200 + D, T=5, H=8, K=64, ctx=160, B=16, D=D, neg_frac=0.3, n_req=2)
+    check_merge_shards(w, list(range(w.T)))
+
+
+@pytest.mark.parametrize("D,I", [(2, 2), (2, 3), (4, 2), (4, 3)])
+def test_convert_dcp_partition_interleaved(D, I):
+    """Page "FlashMLA sparse fp8 path gains DCP and MTP", Implementation breakdown step 4: the
+    interleave argument groups I consecutive tokens per rank."""
+    w = make_random(110 + 10 * D + I, T=6, H=16, K=96, ctx=300, B=16, D=D, neg_frac=0.1, n_req=3, interleave=I)
+    check_convert_partition(w)
+
+
+@pytest.mark.parametrize("D,I", [(2, 2), (2, 3), (4, 2), (4, 3)])
+def test_merge_of_interleaved_shards_equals_unsharded(D, I):
+    w = make_random(210 + 10 * D + I, T=5, H=8, K=64, ctx=161, B=16, D=D, neg_frac=0.3, n_req=2, interleave=I)
     check_merge_shards(w, list(range(w.T)))
 
 

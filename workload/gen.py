@@ -23,9 +23,10 @@ Slots that no valid id may reference carry 0xFF bytes: NaN codes, NaN scales
 and NaN rope, so a read of a wrong slot shows up as NaN.
 
 Placement is constructive: request b's physical slots, in logical order, are the
-concatenated slot ranges of its block-table row.  A DCP shard r (interleave 1)
-holds request b's positions r, r + D, r + 2D, ... in that order, placed through
-the shard's own block table.
+concatenated slot ranges of its block-table row.  A DCP shard r with interleave I
+holds the positions p of request b whose owner (p // I) % D is r, in increasing
+order (local index (p // (I D)) I + p % I), placed through the shard's own block
+table; with I = 1 these are r, r + D, r + 2D, ...
 """
 from __future__ import annotations
 
@@ -160,6 +161,7 @@ class Workload:
     cache: SparseCache
     shards: List[ShardCache]
     note: str = ""
+    interleave: int = 1  # DCP interleave of the shard caches
 
     @property
     def R(self) -> int:
@@ -215,9 +217,10 @@ def _draw_records(rng: np.random.Generator, n: int, kv: str = "fp8_ds_mla") -> n
 class _Builder:
     """Accumulates requests, real positions and records, then places them in caches."""
 
-    def __init__(self, block_size: int, dcp_size: int, record_bytes: int = RECORD_BYTES):
+    def __init__(self, block_size: int, dcp_size: int, record_bytes: int = RECORD_BYTES, interleave: int = 1):
         self.B = block_size
         self.D = dcp_size
+        self.I = interleave
         self.rb = record_bytes
 
     def place(self, ctx, real_pos, records_by_req, bt, nphys, shard_bts):
@@ -234,7 +237,7 @@ class _Builder:
             g_recs.append(recs)
             if D > 1:
                 for r in range(D):
-                    owned = np.arange(r, int(ctx[b]), D)  # global positions held by shard r, local order
+                    owned = _owned_positions(int(ctx[b]), D, self.I, r)  # held by shard r, local order
                     if owned.size == 0:
                         continue
                     local_slots = _slots_in_order(shard_bts[r][0][b], owned.size, B)
@@ -286,23 +289,31 @@ CONFIGS: Dict[int, dict] = {
 
 
 def _finish(name, rng, *, H, K, B, D, out_dtype, ids, req, row_pos, ctx, real_pos, bt_pack, shard_bts, note="",
-            kv="fp8_ds_mla"):
+            kv="fp8_ds_mla", interleave=1):
     T = ids.shape[0]
     q = rng.standard_normal((T, H, HEAD_DIM), dtype=np.float32)
     q_bits = _to_bf16_bits(q)
     recs = _records_for(rng, real_pos, kv)
     bt, nphys = bt_pack
-    cache, shards = _Builder(B, D, KV_KINDS[kv]).place(ctx, real_pos, recs, bt, nphys, shard_bts)
+    cache, shards = _Builder(B, D, KV_KINDS[kv], interleave).place(ctx, real_pos, recs, bt, nphys, shard_bts)
     return Workload(name=name, T=T, H=H, K=K, block_size=B, dcp_size=D, sm_scale=SM_SCALE, out_dtype=out_dtype,
                     q_bits=q_bits, ids=ids.astype(np.int32), req=req.astype(np.int32), row_pos=row_pos.astype(np.int64),
-                    ctx=ctx.astype(np.int64), block_table=bt, cache=cache, shards=shards, note=note)
+                    ctx=ctx.astype(np.int64), block_table=bt, cache=cache, shards=shards, note=note,
+                    interleave=interleave)
 
 
-def _shard_tables(rng, ctx, B, D):
+def _owned_positions(n: int, D: int, I: int, r: int) -> np.ndarray:
+    """Positions p < n that DCP rank r of D holds with interleave I ((p // I) % D == r), in
+    increasing order, which is their local order."""
+    p = np.arange(n)
+    return p[(p // I) % D == r]
+
+
+def _shard_tables(rng, ctx, B, D, I: int = 1):
     out = []
     if D > 1:
         for r in range(D):
-            local_ctx = np.array([len(range(r, int(c), D)) for c in ctx], dtype=np.int64)
+            local_ctx = np.array([_owned_positions(int(c), D, I, r).size for c in ctx], dtype=np.int64)
             out.append(_block_table(rng, -(-local_ctx // B)))
     return out
 
@@ -428,8 +439,8 @@ def _make_c2(kv: str = "fp8_ds_mla") -> Workload:
 
 def make_random(seed: int, *, T: int, H: int, K: int, ctx: int, B: int = 64, D: int = 1, n_req: Optional[int] = None,
                 neg_frac: float = 0.0, valid_max: Optional[int] = None, out_dtype: str = "bf16",
-                all_real: bool = True, spare_blocks: int = 0, kv: str = "fp8_ds_mla") -> Workload:
-    """Small random workload for parity sweeps: ragged -1 patterns, any H/K/D.
+                all_real: bool = True, spare_blocks: int = 0, kv: str = "fp8_ds_mla", interleave: int = 1) -> Workload:
+    """Small random workload for parity sweeps: ragged -1 patterns, any H/K/D and DCP interleave.
 
     Each row draws ``min(K, ctx)`` distinct ids (or ``valid_max``), scatters them over the K
     entries and sets a ``neg_frac`` share of the entries to -1.
@@ -438,7 +449,7 @@ def make_random(seed: int, *, T: int, H: int, K: int, ctx: int, B: int = 64, D: 
     n_req = n_req or T
     ctxs = np.full(n_req, ctx, dtype=np.int64)
     bt_pack = _block_table(rng, -(-ctxs // B), spare_blocks)
-    shard_bts = _shard_tables(rng, ctxs, B, D)
+    shard_bts = _shard_tables(rng, ctxs, B, D, interleave)
     req = np.arange(T) % n_req
     ids = np.full((T, K), -1, dtype=np.int32)
     for t in range(T):
@@ -455,7 +466,8 @@ def make_random(seed: int, *, T: int, H: int, K: int, ctx: int, B: int = 64, D: 
             sel = ids[req == b]
             real.append(np.unique(sel[sel >= 0]))
     return _finish(f"rand{seed}", rng, H=H, K=K, B=B, D=D, out_dtype=out_dtype, ids=ids, req=req,
-                   row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts, kv=kv)
+                   row_pos=row_pos, ctx=ctxs, real_pos=real, bt_pack=bt_pack, shard_bts=shard_bts, kv=kv,
+                   interleave=interleave)
 
 
 def make_dense(seed: int, *, n_req: int, S: int, H: int, ctx, B: int = 64, D: int = 1,
