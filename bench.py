@@ -7,8 +7,10 @@ conversion + decode (fp32 partial out, LSE in the kernel-native (H, T) layout), 
 LSE merge into bf16 out and (T, H) LSE.
 
 Prints one JSON line on stdout.  `value` is query rows per second of the whole step with
-every input resident in HBM.  `roofline` covers the decode kernel: algorithmic bytes and
-flops per launch over its mean launch time (HIP events on the launch stream).
+every input resident in HBM, each step replayed as one HIP graph (`ms_per_step_eager` gives
+the same steps launched one call at a time).  `roofline` covers the decode kernel:
+algorithmic bytes and flops per launch over its mean launch time (HIP events on the launch
+stream around a graph of back-to-back launches).
 `unsharded_decode` times the same rows against the unsharded cache (the H = 128 / top-k 2048
 decode, MFMA-bound) after the step.  `cpu_baseline` times the fp64 oracle on a bounded sample
 of the same rows.  `cache_write` times the fp8_ds_mla cache write of one 32768-token chunk
@@ -285,18 +287,24 @@ def cpu_baseline(w, budget_s, order=None, what=None):
         sub = w.rows(rows)
         q = sub.q_f32()
         outs, lses = [], []
-        for sh in sub.shards:
-            s, _ = O.convert_index(sub.ids, sub.req, sh.block_table, sub.block_size, sub.dcp_size, sh.rank)
-            o, l = O.attention_rows(q, s, sh.cache, sh.cache.num_slots, sub.sm_scale)
-            outs.append(o)
-            lses.append(l)
-        O.merge_lse(np.stack(outs), np.stack(lses))
+        if sub.dcp_size == 1:  # one cache, no merge
+            s, _ = O.convert_index(sub.ids, sub.req, sub.block_table, sub.block_size)
+            O.attention_rows(q, s, sub.cache, sub.cache.num_slots, sub.sm_scale)
+        else:
+            for sh in sub.shards:
+                s, _ = O.convert_index(sub.ids, sub.req, sh.block_table, sub.block_size, sub.dcp_size, sh.rank)
+                o, l = O.attention_rows(q, s, sh.cache, sh.cache.num_slots, sub.sm_scale)
+                outs.append(o)
+                lses.append(l)
+            O.merge_lse(np.stack(outs), np.stack(lses))
         rows_done += len(rows)
     dt = time.perf_counter() - t0
     return {"value": round(rows_done / dt, 3), "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows_done} rows ({what or f'the {w.T} rows of the same DCP{w.dcp_size} step in order'}, "
-                      f"wrapping) through the fp64 numpy oracle: {w.dcp_size} shard converts, shard attention, LSE "
-                      f"merge; {dt:.1f} s on {os.cpu_count()} host CPUs"}
+                      f"wrapping) through the fp64 numpy oracle: "
+                      + ("convert and attention" if w.dcp_size == 1 else
+                         f"{w.dcp_size} shard converts, shard attention, LSE merge")
+                      + f"; {dt:.1f} s on {os.cpu_count()} host CPUs"}
 
 
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
@@ -324,10 +332,148 @@ def measured_traffic():
     return int(t["fetch_bytes"] + t["write_bytes"])
 
 
+def graph_steps(step, q, ids, req, replicas, steps, warmup):
+    """Run the step as HIP graph replays: one captured step per cache replica, `warmup` untimed
+    replays, then exactly `steps` timed replays (replica i % len(replicas) for step i), bracketed
+    by device synchronisation.  Returns the wall time of the timed replays in seconds."""
+    import torch
+    graphs = [step.capture(q, ids, req, shards) for shards in replicas]
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def decode_launch_ms(step, q, replicas, launches=48, rounds=7):
+    """Per-launch decode time: a HIP graph of `launches` back-to-back decode calls (shards and
+    cache replicas in rotation, on the slots of the step's last conversion), replayed `rounds`
+    times between HIP events on the launch stream; one mean per replay.  Back to back, the
+    launches keep the GPU busy, so host-side launch cost stays out of the figure."""
+    import torch
+
+    def body():
+        for k in range(launches):
+            r = k % step.D
+            step.decode_shard(q, replicas[(k // step.D) % len(replicas)][r][0], r)
+
+    body()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    stream = torch.cuda.current_stream()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(rounds):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / launches)
+    return per
+
+
+def achievable_peaks():
+    """What plain loops reach on this device (libsmla_peak.so): streaming HBM read and copy,
+    dense bf16 32x32x16 and fp8 32x32x64 MFMA chains at two waves per SIMD."""
+    from sparse_mla_decode_topk_amd import peak
+    r = peak.run(quick=True)
+    return {"hbm_read_gbps": r["read"]["gbps"], "hbm_copy_gbps": r["copy"]["gbps"],
+            "bf16_mfma_tflops": r["mfma_bf16_32x32x16_w2"]["tflops"], "fp8_mfma_tflops": r["mfma_fp8_32x32x64_w2"]["tflops"],
+            "source": "sparse_mla_decode_topk_amd/peak.py (csrc/peak.hip): streaming read/copy of 1 GiB, "
+                      "8 independent MFMA chains per wave, 8 waves per CU"}
+
+
+def add_achievable(roof, ach):
+    """The fraction of the roofline against the achievable peak of the same unit."""
+    if ach is None:
+        return roof
+    key = "hbm_read_gbps" if roof["unit"] == "GB/s" else "bf16_mfma_tflops"
+    roof["achievable_peak"] = ach[key]
+    roof["frac_of_achievable"] = round(roof["achieved"] / ach[key], 4)
+    return roof
+
+
 def percentiles_us(ms):
     """p10 / median / p90 of launch durations given in milliseconds, in microseconds."""
     import numpy as np
     return [round(float(x) * 1e3, 2) for x in np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])]
+
+
+def main_small(args, cid):
+    """--workload c1 / c2: the small configurations.  c1: 32 single-token decode rows, H = 64,
+    context 4096, top-k 2048, one cache (D = 1; the automatic plan splits every row 8 ways).  c2:
+    the c1 rows plus 4 rows of 2-token contexts, simulated DCP4.  One c1 cache is 86 MB, so
+    `--replicas` (at least 4) copies are rotated between steps to keep the gather in HBM rather
+    than the 256 MB MALL."""
+    import numpy as np
+    import torch
+    import sparse_mla_decode_topk_amd as smla
+    from sparse_mla_decode_topk_amd.pipeline import DcpDecodeStep, device_shards
+    from workload import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    smla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = make_config(cid)
+    reps = max(4, args.replicas)
+    log(f"workload {w.name}: T={w.T} H={w.H} top-k {w.K} D={w.dcp_size}; {reps} cache replicas")
+    q = w.q_torch().to(dev)
+    ids = torch.from_numpy(w.ids).to(dev)
+    req = torch.from_numpy(w.req).to(dev)
+    replicas = [device_shards(w, dev) for _ in range(reps)]
+    torch.cuda.synchronize()
+    step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=w.dcp_size, block_size=w.block_size,
+                         softmax_scale=w.sm_scale, out_dtype=torch.float32, partial_dtype=torch.float32, device=dev)
+    D = w.dcp_size
+    shard_valid = [int(((w.ids >= 0) & (w.ids % D == r)).sum()) for r in range(D)]
+    shard_unique = [unique_records(w.ids, w.req, D, r) for r in range(D)]
+    log(f"warmup {args.warmup} steps (eager), then {args.steps} eager and {args.steps} graph-replayed steps")
+    for i in range(args.warmup):
+        step.run(q, ids, req, replicas[i % reps])
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step.run(q, ids, req, replicas[i % reps])
+    torch.cuda.synchronize()
+    eager_wall = time.perf_counter() - t_start
+    wall = graph_steps(step, q, ids, req, replicas, args.steps, args.warmup)
+    dec_ms = decode_launch_ms(step, q, replicas)
+    mean_dec_s = float(np.mean(dec_ms)) / 1e3
+    byts, flops = decode_algorithmic(w.T, w.H, w.K, float(np.mean(shard_valid)), float(np.mean(shard_unique)),
+                                     out_bytes=4)
+    roof = roofline_entry(byts, flops, mean_dec_s)
+    roof.update({"traffic": None,
+                 "kernel": f"decode_row_kernel (one {'' if D == 1 else f'DCP{D} shard '}call: T={w.T}, H={w.H}, "
+                           f"K={w.K}, fp32 {'out' if D == 1 else 'partials'})",
+                 "launch_us": round(mean_dec_s * 1e6, 2), "launch_us_p10_p50_p90": percentiles_us(dec_ms),
+                 "launch_timing": "mean of back-to-back launches in a HIP graph, events on the launch stream",
+                 "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops)})
+    desc = {1: "c1_decode: 32 requests x 1 token (T=32), H=64, ctx 4096, top-k 2048, fp8_ds_mla cache, D=1 "
+               "(convert + decode, fp32 out)",
+            2: "c2_dcp4: the c1 rows + 4 rows of 2-token contexts (T=36), H=64, top-k 2048, fp8_ds_mla cache, "
+               "simulated DCP4 (convert+decode per shard, LSE merge)"}[cid]
+    line = {
+        "metric": METRIC, "value": round(w.T * args.steps / wall, 1), "unit": "query-rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": desc, "T": w.T, "H": w.H, "topk": w.K, "dcp": D, "block_size": w.block_size,
+                   "cache_replicas": reps, "launch": "each step replayed as one HIP graph"},
+        "ms_per_step_eager": round(eager_wall * 1e3 / args.steps, 4),
+        "kv_gbps": round(656 * float(np.mean(shard_valid)) / mean_dec_s / 1e9, 1),
+        "roofline": add_achievable(roof, None if args.no_peaks else achievable_peaks()),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
 
 
 def main_c4(args):
@@ -358,18 +504,17 @@ def main_c4(args):
                          lse_layout="HT", device=dev)
     shard_valid = [int(((w.ids >= 0) & (w.ids % w.dcp_size == r)).sum()) for r in range(w.dcp_size)]
     shard_unique = [unique_records(w.ids, w.req, w.dcp_size, r) for r in range(w.dcp_size)]
-    stream = torch.cuda.current_stream(dev)
-    log(f"warmup {args.warmup} steps")
+    log(f"warmup {args.warmup} steps (eager), then {args.steps} eager and {args.steps} graph-replayed steps")
     for _ in range(args.warmup):
         step.run(q, ids, req, shards)
     torch.cuda.synchronize()
-    decode_events = []
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        step.run(q, ids, req, shards, decode_events=decode_events)
+        step.run(q, ids, req, shards)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    dec_ms = [a.elapsed_time(b) for a, b in decode_events]
+    eager_wall = time.perf_counter() - t_start
+    wall = graph_steps(step, q, ids, req, [shards], args.steps, args.warmup)
+    dec_ms = decode_launch_ms(step, q, [shards], launches=16, rounds=3)
     mean_dec_s = float(np.mean(dec_ms)) / 1e3
     byts, flops = decode_algorithmic(w.T, w.H, w.K, float(np.mean(shard_valid)), float(np.mean(shard_unique)),
                                      out_bytes=4)
@@ -377,6 +522,7 @@ def main_c4(args):
     roof.update({"traffic": None,
                  "kernel": "decode_row_kernel (one DCP8 shard call: T=4224, H=128, K=2048, fp32 partials)",
                  "launch_us": round(mean_dec_s * 1e6, 2), "launch_us_p10_p50_p90": percentiles_us(dec_ms),
+                 "launch_timing": "mean of back-to-back launches in a HIP graph, events on the launch stream",
                  "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
                  "mfma_frac": round(flops / mean_dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)})
     line = {
@@ -386,8 +532,10 @@ def main_c4(args):
         "config": {"workload": "c4_mixed_dcp8: 128 decode rows (ctx 131072) + 4096 prefill rows (2 x 2048), "
                                "H=128, top-k 2048, fp8_ds_mla cache, simulated DCP8 (convert+decode per shard, "
                                "LSE merge)",
-                   "T": w.T, "H": w.H, "topk": w.K, "dcp": w.dcp_size, "block_size": w.block_size},
-        "kv_gbps": round(656 * sum(shard_valid) * args.steps / (float(np.sum(dec_ms)) / 1e3) / 1e9, 1),
+                   "T": w.T, "H": w.H, "topk": w.K, "dcp": w.dcp_size, "block_size": w.block_size,
+                   "launch": "each step replayed as one HIP graph"},
+        "ms_per_step_eager": round(eager_wall * 1e3 / args.steps, 4),
+        "kv_gbps": round(656 * float(np.mean(shard_valid)) / mean_dec_s / 1e9, 1),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -408,9 +556,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unsharded", action="store_true",
                     help="skip the unsharded decode of the same rows (timed after the step and reported beside it)")
-    ap.add_argument("--workload", choices=("c3", "dense", "bf16", "c4"), default="c3",
-                    help="c3: the DCP2 MTP step (default); dense: the whole-context MTP decode; bf16: the c3 rows "
-                         "unsharded against a plain bf16 cache; c4: the long-context mixed batch under DCP8")
+    ap.add_argument("--workload", choices=("c3", "c1", "c2", "dense", "bf16", "c4"), default="c3",
+                    help="c3: the DCP2 MTP step (default); c1 / c2: the small single-token decode batch, unsharded / "
+                         "under DCP4; dense: the whole-context MTP decode; bf16: the c3 rows unsharded against a plain "
+                         "bf16 cache; c4: the long-context mixed batch under DCP8")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak microbenchmarks")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -426,6 +576,9 @@ def main():
         return
     if args.workload == "c4":
         main_c4(args)
+        return
+    if args.workload in ("c1", "c2"):
+        main_small(args, int(args.workload[1]))
         return
 
     import numpy as np
@@ -464,33 +617,25 @@ def main():
         shard_valid.append(int(own.sum()))
         shard_unique.append(unique_records(w.ids, w.req, w.dcp_size, r))
 
-    decode_events = []  # (start, end) events around every decode launch, on the launch stream
-    stream = torch.cuda.current_stream(dev)
+    def run_step(i):
+        return step.run(q, ids, req, replicas[i % len(replicas)])
 
-    def run_step(i, events=None):
-        return step.run(q, ids, req, replicas[i % len(replicas)], decode_events=events)
-
-    log(f"warmup {args.warmup} steps")
+    log(f"warmup {args.warmup} steps (eager), then {args.steps} eager and {args.steps} graph-replayed steps")
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start = time.perf_counter()
-    ev0.record(stream)
     for i in range(args.steps):
-        run_step(i, decode_events)
-    ev1.record(stream)
+        run_step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    gpu_ms = ev0.elapsed_time(ev1)
-    dec_ms = [a.elapsed_time(b) for a, b in decode_events]
+    eager_wall = time.perf_counter() - t_start
+    wall = graph_steps(step, q, ids, req, replicas, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = w.T * args.steps / wall
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {gpu_ms / args.steps:.4f} ms/step events")
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (graph), {eager_wall * 1e3 / args.steps:.4f} (eager)")
 
-    # decode kernel roofline: mean over the timed launches (both shards have ~the same valid count)
+    # decode kernel roofline: mean over back-to-back launches (both shards have ~the same valid count)
+    dec_ms = decode_launch_ms(step, q, replicas)
     mean_dec_s = float(np.mean(dec_ms)) / 1e3
     nv_mean = float(np.mean(shard_valid))
     byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, float(np.mean(shard_unique)), out_bytes=4)
@@ -499,22 +644,18 @@ def main():
     roof["kernel"] = "decode_row_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
     roof["launch_us"] = round(mean_dec_s * 1e6, 2)
     roof["launch_us_p10_p50_p90"] = percentiles_us(dec_ms)
+    roof["launch_timing"] = "mean of back-to-back launches in a HIP graph, events on the launch stream"
     roof["algorithmic_bytes"] = int(byts)
     roof["algorithmic_flops"] = int(flops)
-    kv_gbps = 656 * sum(shard_valid) * args.steps / (float(np.sum(dec_ms)) / 1e3) / 1e9
+    kv_gbps = 656 * float(np.mean(shard_valid)) / mean_dec_s / 1e9
 
     unsharded = None
     if not args.no_unsharded:  # the unsharded H=128 / top-k 2048 decode of the same rows
         one = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=1, block_size=w.block_size, softmax_scale=w.sm_scale,
                             out_dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            one.run(q, ids, req, [(unsharded_cache, unsharded_bt)])
+        one.run(q, ids, req, [(unsharded_cache, unsharded_bt)])
         torch.cuda.synchronize()
-        un_events = []
-        for _ in range(max(10, args.steps // 2)):
-            one.run(q, ids, req, [(unsharded_cache, unsharded_bt)], decode_events=un_events)
-        torch.cuda.synchronize()
-        un_ms = [a.elapsed_time(b) for a, b in un_events]
+        un_ms = decode_launch_ms(one, q, [[(unsharded_cache, unsharded_bt)]], launches=24)
         un_s = float(np.mean(un_ms)) / 1e3
         ub, uf = decode_algorithmic(w.T, w.H, w.K, nvalid[0], unique_records(w.ids, w.req), out_bytes=2)
         unsharded = {"decode_us": round(un_s * 1e6, 2), "decode_us_p10_p50_p90": percentiles_us(un_ms),
@@ -537,12 +678,18 @@ def main():
         "config": {"workload": "c3_mtp_dcp2: 64 req x 4 MTP tokens (T=256), H=128, top-k 2048 causal, ctx 32768, "
                                "fp8_ds_mla cache, simulated DCP2 (convert+decode per shard, LSE merge)",
                    "T": w.T, "H": w.H, "topk": w.K, "ctx": 32768, "dcp": w.dcp_size, "block_size": w.block_size,
-                   "cache_replicas": len(replicas)},
+                   "cache_replicas": len(replicas), "launch": "each step replayed as one HIP graph"},
+        "ms_per_step_eager": round(eager_wall * 1e3 / args.steps, 4),
         "kv_gbps": round(kv_gbps, 1),
         "roofline": roof,
     }
+    ach = None if args.no_peaks else achievable_peaks()
+    add_achievable(line["roofline"], ach)
     if unsharded is not None:
+        add_achievable(unsharded["roofline"], ach)
         line["unsharded_decode"] = unsharded
+    if ach is not None:
+        line["achievable_peaks"] = ach
     line["cache_write"] = cache_write
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -144,10 +144,11 @@ size_t sparse_mla_decode_workspace_size(int32_t T, int32_t H, int32_t K, int32_t
  *          (H,1), or the kernel-native (H,T) layout with strides (1,T) ([P-FlashMLA]
  *          "Implementation breakdown" step 1).
  * num_splits  0 = automatic; otherwise the number of top-k ranges each row is cut
- *          into (1..64), combined inside the kernel through the workspace.
+ *          into (1..64).  With more than one, the decode kernel leaves fp32 partials
+ *          in the workspace and a second kernel on the same stream merges them.
  * workspace   device memory of at least sparse_mla_decode_workspace_size(T,H,K,
- *          num_splits) bytes, 256-byte aligned, any contents (the call initialises
- *          what it needs with a kernel of its own); may be NULL when the size is 0.
+ *          num_splits) bytes, 256-byte aligned, any contents (every byte read is
+ *          written first by the same call); may be NULL when the size is 0.
  *          Calls that share a workspace must be ordered (same stream); concurrent
  *          ones race.
  * Supported: 1 <= H <= 128, H % 16 == 0; K <= 4096 * num_splits (automatic splits
@@ -164,16 +165,16 @@ int sparse_mla_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, con
  * sparse_mla_decode_noalloc - sparse_mla_decode without a workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation.  The call allocates nothing and calls no allocating routine; its split
- * partials and arrival counters live in a scratch array the library holds on each device it runs
- * on (SMLA_NOALLOC_SCRATCH_BYTES, kept until the process ends).
+ * partials live in a scratch array the library holds on each device it runs on
+ * (SMLA_NOALLOC_SCRATCH_BYTES, kept until the process ends).
  *
  * Arguments, layouts, results and errors are those of sparse_mla_decode (same kernels, same
  * split plan), except: the workspace is the library's scratch array; a call whose split plan
  * needs more than SMLA_NOALLOC_SCRATCH_BYTES (see sparse_mla_decode_workspace_size) returns
  * SMLA_ERR_WORKSPACE and launches nothing; SMLA_ERR_HIP if the runtime cannot give the scratch
- * array's device address.  Every call on one device shares that device's array, and each call
- * clears the counters it needs, so calls on one device must not overlap in time (calls on
- * different streams of one device race).
+ * array's device address.  Every call on one device shares that device's array (each call
+ * writes every byte of it that it reads), so calls on one device must not overlap in time
+ * (calls on different streams of one device race).
  */
 int sparse_mla_decode_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h, const uint8_t* kv_cache,
                               int64_t num_slots, const int32_t* slots, int64_t slots_ld, const int32_t* valid_count,

@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsmla.so")
 PEAK_LIB = os.path.join(PKG, "libsmla_peak.so")
 SOURCES = ["smla_api.hip", "convert_index.hip", "decode_row.hip", "merge_lse.hip", "cache_write.hip", "dense_slots.hip",
-           "decode_bf16.hip"]
+           "decode_bf16.hip", "split_combine.hip"]
 EXTRA_FLAGS = {"decode_row.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("SMLA_OFFLOAD_ARCH", "gfx950")
 COMMON = ["-O3", "-std=c++17", "-fPIC",

@@ -24,7 +24,8 @@
 //  * PV on v_mfma_f32_32x32x16_bf16: O^T[dim, head] += V^T[dim, token] . P^T[token, head];
 //    the V^T operand comes straight from the staged tile through two ds_read_b64_tr_b16 per
 //    32-dim block (lane i of a 16-lane group receives dim D0 + i of four consecutive tokens).
-//  * One LDS-only barrier per tile; split-K arrival and merge as in the fp8 kernel.
+//  * One LDS-only barrier per tile; split-K partials merged by the split-merge kernel as in the
+//    fp8 kernel.
 
 #include "decode_common.h"
 
@@ -53,7 +54,6 @@ constexpr int kPSpan = 2 * kPTile > kOutStageBytes - kStages * kTileBytes - 4 * 
 
 static_assert(kRecB % 64 == 0, "a copy moves four whole chunks");
 static_assert(kAhead == 4, "load waits below are written for 4 tiles ahead");
-static_assert(kHB * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile buffers");
 
 struct Shared {
   uint8_t stage[kStages * kTileBytes];  // followed directly by pbuf and clist: the output staging
@@ -61,7 +61,6 @@ struct Shared {
   int32_t clist[kMaxEntriesPerSplit];
   float ml[2 * kHB];  // per head of the block: (reference max, sum)
   int32_t wave_cnt[kThreads / 64];
-  int32_t last_flag;
 };
 static_assert(offsetof(Shared, pbuf) == offsetof(Shared, stage) + sizeof(Shared::stage) &&
                   offsetof(Shared, clist) == offsetof(Shared, pbuf) + sizeof(Shared::pbuf) &&
@@ -304,13 +303,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p
     value_role(p, sh, bk, wave - 4, lane);
   __syncthreads();  // output rows staged
   store_rows(p, bk, staging(sh), tid);
-  if (p.splits == 1) return;
-  if (arrive_last(p, bk, sh, tid)) combine_splits(p, bk, sh, reinterpret_cast<float*>(sh.stage), tid);
-}
-
-__global__ void zero_counters_bf16(int32_t* cnt, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) cnt[i] = 0;
 }
 
 }  // namespace
@@ -318,13 +310,10 @@ __global__ void zero_counters_bf16(int32_t* cnt, int64_t n) {
 hipError_t launch_decode_bf16(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
   const int64_t items = (int64_t)p.T * plan.head_blocks * plan.splits;
   const unsigned grid = (unsigned)((items + 7) / 8 * 8);
-  if (plan.splits > 1) {
-    // arrival counters start at zero on every call (a kernel, not a memset node)
-    const int64_t n = (int64_t)p.T * plan.head_blocks;
-    hipLaunchKernelGGL(zero_counters_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.ws_cnt, n);
-  }
   hipLaunchKernelGGL(decode_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  return launch_split_combine(p, stream);
 }
 
 }  // namespace smla

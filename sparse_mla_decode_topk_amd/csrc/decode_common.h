@@ -103,13 +103,13 @@ __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
   return true;
 }
 
-// A row the caller marks empty through its valid count (<= 0): the first split of the row
-// writes out = 0 and lse = -inf for the block's heads; neither q nor the slot list is read.
-// Returns true when the workgroup is done.
+// A row the caller marks empty through its valid count (<= 0): neither q nor the slot list is
+// read.  Unsplit, the workgroup writes out = 0 and lse = -inf for the block's heads; split, it
+// does nothing (the split merge writes the row).  Returns true when the workgroup is done.
 template <int NT>
 __device__ __forceinline__ bool skip_marked_empty(const DecodeParams& p, const Block& bk, int tid) {
   if (p.valid == nullptr || p.valid[bk.row] > 0) return false;
-  if (bk.split != 0) return true;
+  if (p.splits > 1) return true;
   const int per_row = p.out_fp32 ? 4 * kLatent / 16 : 2 * kLatent / 16;  // 16-byte pieces of one head
   for (int c = tid; c < bk.nh * per_row; c += NT) {
     const int h = bk.h_lo + c / per_row, col = c % per_row;
@@ -275,99 +275,6 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
     __syncthreads();
   }
   return total;
-}
-
-// The last split of a (row, head block) to arrive merges every split's partial.  First one
-// thread per head turns the splits' (max, sum) into normalised weights in LDS (and writes the
-// head's LSE); then, CH heads at a time, each thread owns 4 dims of every (NT / 128)-th head and,
-// split by split, loads all of its partial rows before accumulating them, so the merge costs
-// one memory round trip per split rather than several per output element.  `wts` needs
-// HB * splits floats of LDS.
-template <class SH, int NT = kThreads, int HB = kHB>
-__device__ __forceinline__ void combine_splits(const DecodeParams& p, const Block& bk, SH& sh, float* wts, int tid) {
-  for (int hl = tid; hl < bk.nh; hl += NT) {
-    const int h = bk.h_lo + hl;
-    const float* ml = p.ws_ml + ((int64_t)bk.row * p.splits * p.H + h) * 2;  // split sp at + sp * H * 2
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2));
-    float L = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int sp = 0; sp < p.splits; ++sp) {
-        const float ms = __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2);
-        const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
-        wts[hl * p.splits + sp] = w;
-        L += w * __builtin_nontemporal_load(ml + (int64_t)sp * p.H * 2 + 1);
-      }
-    }
-    const bool empty = !(L > 0.0f);
-    const float inv = empty ? 0.0f : 1.0f / L;
-    for (int sp = 0; sp < p.splits; ++sp) wts[hl * p.splits + sp] = empty ? 0.0f : wts[hl * p.splits + sp] * inv;
-    p.lse[(int64_t)bk.row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
-  }
-  __syncthreads();
-  constexpr int kHeadStep = NT / (kLatent / 4);  // heads one pass of the threads covers
-  constexpr int kPerThread = 16;                 // (head, 4-dim) items per thread and chunk
-  constexpr int CH = kHeadStep * kPerThread;     // heads per chunk
-  static_assert(HB % CH == 0 || CH >= HB, "head chunks");
-  const int d4 = tid % (kLatent / 4);
-  const int h0 = tid / (kLatent / 4);  // heads h0, h0 + kHeadStep, ... of the chunk (wave-uniform)
-#pragma unroll 1
-  for (int hc = 0; hc < HB; hc += CH) {
-    f32x4 acc[kPerThread];
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < p.splits; ++sp) {
-      f32x4 part[kPerThread];
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int hl = hc + h0 + kHeadStep * i;
-        part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (hl < bk.nh && wts[hl * p.splits + sp] != 0.0f) {
-          const int64_t pidx = ((int64_t)bk.row * p.splits + sp) * p.H + bk.h_lo + hl;
-          part[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ws_o + pidx * kLatent) + d4);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int hl = hc + h0 + kHeadStep * i;
-        if (hl < bk.nh) acc[i] += wts[hl * p.splits + sp] * part[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int hl = hc + h0 + kHeadStep * i;
-      if (hl >= bk.nh) continue;
-      const int h = bk.h_lo + hl;
-      if (p.out_fp32) {
-        float* orow = reinterpret_cast<float*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-        *reinterpret_cast<f32x4*>(orow + 4 * d4) = acc[i];
-      } else {
-        __bf16* orow = reinterpret_cast<__bf16*>(p.out) + (int64_t)bk.row * p.o_st + (int64_t)h * p.o_sh;
-        *reinterpret_cast<bf16x4*>(orow + 4 * d4) =
-            bf16x4{(__bf16)acc[i][0], (__bf16)acc[i][1], (__bf16)acc[i][2], (__bf16)acc[i][3]};
-      }
-    }
-  }
-}
-
-// Split-K arrival: true in the last split of this (row, head block) to arrive, which then
-// merges all of them.  The barrier completes every wave's partial stores; one device-scope
-// acquire-release atomic by one thread then publishes them and, in the last split, makes the
-// other splits' partials visible to the workgroup after the second barrier.  (A device-scope
-// fence in every thread would make each wave write back the L2 of its XCD: measured twice as
-// slow.)
-template <class SH>
-__device__ __forceinline__ bool arrive_last(const DecodeParams& p, const Block& bk, SH& sh, int tid) {
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.ws_cnt + (int64_t)bk.row * p.head_blocks + bk.hb, 1, __ATOMIC_ACQ_REL,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    sh.last_flag = old == p.splits - 1;
-  }
-  __syncthreads();
-  return sh.last_flag != 0;
 }
 
 }  // namespace dec

@@ -42,8 +42,8 @@
 //    at position r ^ 8 and odd scale rows token r at r ^ 8, so the transposed value reads of two
 //    lane groups fall in different banks.
 //  * Output rows are staged through LDS and written as whole rows.  Split-K over the top-k list
-//    with an in-kernel combine (last split to arrive merges); a row with no valid entry yields
-//    out = 0, lse = -inf.
+//    leaves fp32 partials and (max, sum) pairs that a second kernel merges (split_combine.hip);
+//    a row with no valid entry yields out = 0, lse = -inf.
 
 #include "decode_common.h"
 
@@ -68,7 +68,6 @@ constexpr int kStg16 = 2 * kLatent + 16;              //   (16 bytes of padding:
 
 static_assert(kRH == 64, "score waves: 2 token halves x 2 head halves of 32; output blocks of 32 heads");
 static_assert(kStages == kAhead + 2, "ring: the tile being scored, the one being valued, the copies");
-static_assert(kRH * kMaxSplits * 4 <= kStages * kTileBytes, "split weights fit in the tile ring");
 static_assert(32 * kStg32 <= kStages * kTileBytes && 64 * kStg16 <= kStages * kTileBytes, "output staging fits");
 
 struct RowShared {
@@ -77,7 +76,6 @@ struct RowShared {
   int32_t clist[kMaxEntriesPerSplit];
   float xch[2][kRH];  // per token half: the block's per-head maxima or sums, exchanged between halves
   int32_t wave_cnt[kRT / 64];
-  int32_t last_flag;
 };
 
 // Position of record r in chunk row c of a tile, and of token r in scale row t.
@@ -574,14 +572,6 @@ __global__ __launch_bounds__(kRT, 1) void decode_row_kernel(DecodeParams p) {
   bk.ntiles = (bk.total + kTT - 1) / kTT;
   if (w < 4) score_role<kFull>(p, bk, sh, w, lane);
   else value_role(p, bk, sh, w - 4, lane);
-  if (p.splits == 1) return;
-  if (arrive_last(p, bk, sh, tid))
-    combine_splits<RowShared, kRT, kRH>(p, bk, sh, reinterpret_cast<float*>(sh.stage), tid);
-}
-
-__global__ void zero_row_counters(int32_t* cnt, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) cnt[i] = 0;
 }
 
 }  // namespace
@@ -589,15 +579,13 @@ __global__ void zero_row_counters(int32_t* cnt, int64_t n) {
 hipError_t launch_decode_row(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
   const int64_t items = (int64_t)p.T * plan.head_blocks * plan.splits;
   const unsigned grid = (unsigned)((items + 7) / 8 * 8);
-  if (plan.splits > 1) {
-    const int64_t n = (int64_t)p.T * plan.head_blocks;
-    hipLaunchKernelGGL(zero_row_counters, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.ws_cnt, n);
-  }
   if (p.H % kRH == 0)
     hipLaunchKernelGGL(decode_row_kernel<true>, dim3(grid), dim3(kRT), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_row_kernel<false>, dim3(grid), dim3(kRT), 0, stream, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  return launch_split_combine(p, stream);
 }
 
 }  // namespace smla

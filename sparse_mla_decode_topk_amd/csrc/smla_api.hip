@@ -57,9 +57,8 @@ DecodePlan make_plan(int32_t T, int32_t H, int32_t K, int32_t num_splits, int cu
   if (splits > 1) {
     pl.ws_o_bytes = round_up((size_t)T * splits * H * kLatent * sizeof(float), 256);
     pl.ws_ml_bytes = round_up((size_t)T * splits * H * 2 * sizeof(float), 256);
-    pl.ws_cnt_bytes = round_up((size_t)T * pl.head_blocks * sizeof(int32_t), 256);
   }
-  pl.ws_total = pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_cnt_bytes;
+  pl.ws_total = pl.ws_o_bytes + pl.ws_ml_bytes;
   return pl;
 }
 
@@ -191,9 +190,8 @@ int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const 
   p.heads_per_block = hpb;
   if (plan.ws_total > 0) {
     char* ws = static_cast<char*>(workspace);
-    p.ws_cnt = reinterpret_cast<int32_t*>(ws);
-    p.ws_ml = reinterpret_cast<float*>(ws + plan.ws_cnt_bytes);
-    p.ws_o = reinterpret_cast<float*>(ws + plan.ws_cnt_bytes + plan.ws_ml_bytes);
+    p.ws_ml = reinterpret_cast<float*>(ws);
+    p.ws_o = reinterpret_cast<float*>(ws + plan.ws_ml_bytes);
   }
   return SMLA_OK;
 }

@@ -49,7 +49,6 @@ struct DecodeParams {
   int32_t splits, entries_per_split, head_blocks, heads_per_block;
   float* ws_o;    // [T, splits, H, 512] unnormalised partial outputs
   float* ws_ml;   // [T, splits, H, 2]   (running max in log2 units, sum)
-  int32_t* ws_cnt;  // [T, head_blocks] arrival counters, left at zero
 };
 
 struct MergeParams {
@@ -96,12 +95,14 @@ struct DecodePlan {
   int32_t head_blocks;  // workgroups per row along heads
   int32_t splits;       // top-k ranges per row
   int32_t entries_per_split;
-  size_t ws_o_bytes, ws_ml_bytes, ws_cnt_bytes, ws_total;
+  size_t ws_o_bytes, ws_ml_bytes, ws_total;
 };
 
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_decode_row(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream);
+// The merge of a split decode's partials (p.splits > 1) into out and lse.
+hipError_t launch_split_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_dense_slots(const DenseSlotParams& p, hipStream_t stream);

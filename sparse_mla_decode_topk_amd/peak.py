@@ -79,8 +79,8 @@ def _check(st, what):
         raise RuntimeError(f"{what}: status {st}")
 
 
-def run(mib: int = 1024, iters: int = 4096, cus: int | None = None) -> dict:
-    """All measurements; returns a JSON-ready dict."""
+def run(mib: int = 1024, iters: int = 4096, cus: int | None = None, quick: bool = False) -> dict:
+    """All measurements; returns a JSON-ready dict.  quick: only the streams and the MFMA chains."""
     lib = load()
     dev = torch.device("cuda", torch.cuda.current_device())
     cus = cus or torch.cuda.get_device_properties(dev).multi_processor_count
@@ -111,6 +111,9 @@ def run(mib: int = 1024, iters: int = 4096, cus: int | None = None) -> dict:
             peak = PUBLISHED["fp8_tflops" if kind == 2 else "bf16_tflops"]
             res[f"mfma_{name}_w{wps}"] = {"tflops": round(tf, 1), "frac_of_published": round(tf / peak, 3),
                                           "us": round(ms * 1e3, 1)}
+
+    if quick:
+        return res
 
     # MFMA + independent fp32 FMAs in one wave: time per iteration (four 32x32x16 bf16 MFMAs), with
     # the FMAs after the four MFMAs (mix) or spread between them (mixi)

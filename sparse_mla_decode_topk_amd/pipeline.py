@@ -1,7 +1,7 @@
 """One decode step of the sparse-MLA path with simulated DCP shards on one GPU.
 
 Chains the three library calls with buffers allocated once up front (no allocation,
-no host synchronisation inside ``run``, so a step can be captured in a HIP graph):
+no host synchronisation inside ``run``, so ``capture`` can record a step as a HIP graph):
 
     for each shard r:  sparse_mla_convert_index(ids -> shard-local slots, -1 in place)
                        sparse_mla_decode(q, shard cache, slots -> partial out, lse)
@@ -55,23 +55,44 @@ class DcpDecodeStep:
             raise ValueError("one (cache, block table) pair per shard")
         stream = torch.cuda.current_stream(q.device)
         for r, (cache, bt) in enumerate(shards):
-            sl, vc = B.convert_index(ids, req, bt, self.block_size, dcp_size=self.D, dcp_rank=r,
-                                     interleave=self.interleave, out=self.slots[r], valid=self.valid[r])
+            B.convert_index(ids, req, bt, self.block_size, dcp_size=self.D, dcp_rank=r, interleave=self.interleave,
+                            out=self.slots[r], valid=self.valid[r])
             if decode_events is not None:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record(stream)
-            if self.D == 1:
-                B.decode(q, cache, self.slots[r], self.scale, out=self.out, lse=self.lse, num_splits=self.num_splits,
-                         workspace=self.workspace, valid_count=vc)
-            else:
-                B.decode(q, cache, self.slots[r], self.scale, out=self.parts[r], lse=self.lse_parts[r],
-                         num_splits=self.num_splits, workspace=self.workspace, valid_count=vc)
+            self.decode_shard(q, cache, r)
             if decode_events is not None:
                 ev[1].record(stream)
                 decode_events.append(ev)
         if self.D > 1:
             B.merge_lse(self.parts, self.lse_parts, out=self.out, lse=self.lse)
         return self.out, self.lse
+
+    def decode_shard(self, q: torch.Tensor, cache: torch.Tensor, r: int) -> None:
+        """The decode of shard r alone, from the slots and counts its last conversion left."""
+        if self.D == 1:
+            B.decode(q, cache, self.slots[r], self.scale, out=self.out, lse=self.lse, num_splits=self.num_splits,
+                     workspace=self.workspace, valid_count=self.valid[r])
+        else:
+            B.decode(q, cache, self.slots[r], self.scale, out=self.parts[r], lse=self.lse_parts[r],
+                     num_splits=self.num_splits, workspace=self.workspace, valid_count=self.valid[r])
+
+    def capture(self, q: torch.Tensor, ids: torch.Tensor, req: torch.Tensor,
+                shards: Sequence[Tuple[torch.Tensor, torch.Tensor]]) -> "torch.cuda.CUDAGraph":
+        """Record one run() over these tensors as a HIP graph.
+
+        Each replay re-runs the whole step (every conversion, decode and the merge) on the same
+        storage: change the inputs' contents in place between replays, never their storage.
+        Results land in self.out / self.lse.  The graph holds kernel nodes only (no memset or
+        copy nodes), and one graph must not be replayed on two streams at once, since the
+        replays share this step's buffers.
+        """
+        self.run(q, ids, req, shards)  # outside the capture: first-use work of the binding and torch
+        torch.cuda.synchronize(q.device)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(q, ids, req, shards)
+        return graph
 
 
 def device_shards(workload, device="cuda") -> List[Tuple[torch.Tensor, torch.Tensor]]:

@@ -1,6 +1,6 @@
 """The cache write, the whole-context decode and the bf16-record decode captured in one HIP graph:
-every replay equals the eager result (the calls allocate nothing, synchronise nothing and clear
-their counters with a kernel, so the graph can be replayed as is)."""
+every replay equals the eager result (the calls allocate nothing, synchronise nothing and record
+kernel nodes only, so the graph can be replayed as is)."""
 import numpy as np
 import pytest
 import torch

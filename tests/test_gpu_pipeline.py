@@ -169,21 +169,13 @@ def test_graph_capture_replays_match_eager():
     w = make_random(401, T=12, H=128, K=512, ctx=2048, B=64, D=2, neg_frac=0.1, n_req=3)
     shards = device_shards(w)
     q, ids, req = q_dev(w), dev(w.ids), dev(w.req)
-    for num_splits in (1, 3):  # 3 exercises the workspace and the counter-zeroing kernel
+    for num_splits in (1, 3):  # 3 exercises the workspace and the split-merge kernel
         step = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=2, block_size=w.block_size, softmax_scale=w.sm_scale,
                              num_splits=num_splits)
         out, lse = step.run(q, ids, req, shards)
         torch.cuda.synchronize()
         eager_o, eager_l = out.clone(), lse.clone()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step.run(q, ids, req, shards)  # warm up on the capture stream
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step.run(q, ids, req, shards)
+        g = step.capture(q, ids, req, shards)
         for rep in range(3):
             step.out.fill_(123.0)
             step.lse.fill_(-5.0)
@@ -194,3 +186,14 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(step.lse, eager_l), f"replay {rep} splits {num_splits}: lse differs"
         ref_o, ref_l = oracle_unsharded(w)
         check_close(step.out, step.lse, ref_o, ref_l, what=f"graph splits{num_splits}")
+        # new contents in the captured storage: the replay reads them, and matches an eager run
+        q2 = q.clone()
+        q.mul_(-0.5)
+        g.replay()
+        torch.cuda.synchronize()
+        graph_o, graph_l = step.out.clone(), step.lse.clone()
+        step.run(q, ids, req, shards)
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, graph_o) and torch.equal(step.lse, graph_l), f"splits {num_splits}: new q"
+        assert not torch.equal(graph_o, eager_o)
+        q.copy_(q2)

@@ -114,11 +114,11 @@ def test_decode_validation(lib, kw, want):
 
 
 def test_workspace_size(lib):
-    # one split needs nothing; s splits need counters, (max, sum) and fp32 partial outputs
+    # one split needs nothing; s splits need (max, sum) pairs and fp32 partial outputs
     assert lib.sparse_mla_decode_workspace_size(256, 128, 2048, 1) == 0
     T, H, K, S = 32, 64, 2048, 8
     r = lambda x: (x + 255) // 256 * 256
-    want = r(T * 1 * 4) + r(T * S * H * 2 * 4) + r(T * S * H * 512 * 4)
+    want = r(T * S * H * 2 * 4) + r(T * S * H * 512 * 4)
     assert lib.sparse_mla_decode_workspace_size(T, H, K, S) == want
     assert lib.sparse_mla_decode_workspace_size(0, 64, 2048, 0) == 0
     assert lib.sparse_mla_decode_workspace_size(4, 64, -1, 0) == 0
