@@ -538,6 +538,24 @@ def main_c4(args):
         "kv_gbps": round(656 * float(np.mean(shard_valid)) / mean_dec_s / 1e9, 1),
         "roofline": roof,
     }
+    if not args.no_bf16_partials:  # the same step with bf16 shard partials: time and distance
+        out32, lse32 = step.out.float().clone(), step.lse.clone()
+        del step
+        step16 = DcpDecodeStep(T=w.T, H=w.H, K=w.K, dcp_size=w.dcp_size, block_size=w.block_size,
+                               softmax_scale=w.sm_scale, out_dtype=torch.bfloat16, partial_dtype=torch.bfloat16,
+                               lse_layout="HT", device=dev)
+        wall16 = graph_steps(step16, q, ids, req, [shards], args.steps, args.warmup)
+        dec16 = decode_launch_ms(step16, q, [shards], launches=16, rounds=3)
+        fin = torch.isfinite(lse32)
+        d_out = float((step16.out.float() - out32).abs().max())
+        d_lse = float((step16.lse[fin] - lse32[fin]).abs().max()) if bool(fin.any()) else 0.0
+        same_inf = bool(torch.equal(torch.isneginf(step16.lse), torch.isneginf(lse32)))
+        line["bf16_partials"] = {
+            "ms_per_step": round(wall16 * 1e3 / args.steps, 4), "launch_us": round(float(np.mean(dec16)) * 1e3, 2),
+            "max_abs_dout_vs_fp32_partials": d_out, "max_abs_dlse_vs_fp32_partials": d_lse,
+            "neg_inf_lse_identical": same_inf, "out_tolerance": 2e-2, "out_margin": round(2e-2 / d_out, 1) if d_out else None,
+            "note": "the same step with bf16 shard partials (decode writes bf16, the merge reads bf16); distances "
+                    "are to the fp32-partial step of this run, every element"}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         order = np.random.Generator(np.random.PCG64(4004)).permutation(w.T)
@@ -561,6 +579,7 @@ def main():
                          "under DCP4; dense: the whole-context MTP decode; bf16: the c3 rows unsharded against a plain "
                          "bf16 cache; c4: the long-context mixed batch under DCP8")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak microbenchmarks")
+    ap.add_argument("--no-bf16-partials", action="store_true", help="c4: skip the bf16-partial variant of the step")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

@@ -173,9 +173,9 @@ def test_decode_late_dominant_score_exceeds_headroom(kv, splits):
 
 @pytest.mark.parametrize("splits", [1, 3])
 def test_decode_query_ranges_per_head(splits):
-    """Heads of q scaled by powers of two from 2^-110 to 2^3, and one all-zero head: the
-    per-head range factor of the query split (2^e with max |q 2^e| near 448, clamped to
-    |e| <= 100) is taken back out by the fp8 MFMA's per-row scale, so every head must match."""
+    """Heads of q scaled by powers of two from 2^-110 to 2^3, and one all-zero head: q enters the
+    score products as given (bf16), so tiny and zero heads must match as well as the others (their
+    scores sit near 0 and their softmax is nearly uniform)."""
     import dataclasses
 
     w = make_random(91, T=5, H=64, K=300, ctx=700, B=64, neg_frac=0.1, n_req=2)
@@ -216,8 +216,8 @@ def test_decode_longest_list():
 def _wide_range_q(w, seed):
     """q whose values inside each head span a wide range: one or two dims per (row, head) at
     +-2^5 .. 2^7 and every other dim +-2^u with u uniform in [-14, -2], all exact in bf16.  Small
-    values next to a large one are where a split of q into two e4m3 terms under one range factor
-    per head stops being exact."""
+    values next to a large one are where any narrower encoding of q (two e4m3 terms under one
+    range factor per head, say) stops being exact; the bf16 score products must not care."""
     import dataclasses
 
     rng = np.random.default_rng(seed)

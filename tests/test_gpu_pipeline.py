@@ -117,14 +117,16 @@ def test_dcp8_c4_subset_rows_full_caches():
     print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
 
 
-def test_dcp8_c4_full_size_rows():
+@pytest.mark.parametrize("partials", [torch.float32, torch.bfloat16])
+def test_dcp8_c4_full_size_rows(partials):
     """The mixed batch at its full size (T = 4224, 8 shards), in the launch the c4 bench line times,
     against the oracle on every decode row, every prefill row at positions 0-63 (a row at position p
     has p + 1 candidates, so up to 7 of its 8 shards own none and must drop out of the merge) and a
-    sample further along both prompts."""
+    sample further along both prompts; with fp32 shard partials (the default) and with bf16 ones
+    (one more rounding of every partial row before the merge)."""
     w = make_config(4)
-    print(f"c4 full: T={w.T} H={w.H} D={w.dcp_size}", flush=True)
-    step, out, lse = run_step(w, lse_layout="HT")
+    print(f"c4 full: T={w.T} H={w.H} D={w.dcp_size} partials {partials}", flush=True)
+    step, out, lse = run_step(w, lse_layout="HT", partial_dtype=partials)
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
     pos = np.asarray(w.row_pos)
     decode_rows = [int(r) for r in np.flatnonzero(pos == pos.max())]
