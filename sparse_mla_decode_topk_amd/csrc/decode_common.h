@@ -232,8 +232,7 @@ __device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& b
 template <class SH, int NT = kThreads>
 __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block& bk, SH& sh, int tid, int wave,
                                              int lane) {
-  constexpr int kPer = kMaxEntriesPerSplit / NT;
-  static_assert(kPer % 4 == 0, "entries per thread come in groups of four");
+  constexpr int kPer = ((kMaxEntriesPerSplit + NT - 1) / NT + 3) / 4 * 4;  // groups of four per thread
   const int e0 = bk.split * p.entries_per_split;
   const int e1 = min(p.K, e0 + p.entries_per_split);
   const int32_t* srow = p.slots + (int64_t)bk.row * p.slots_ld;

@@ -40,6 +40,9 @@ class DcpDecodeStep:
             else:
                 self.lse_store = torch.empty((dcp_size, T, H), dtype=torch.float32, device=dev)
                 self.lse_parts = self.lse_store
+        if num_splits == 0 and dcp_size > 1:  # plan the shard decodes for their ~K / D valid entries
+            num_splits = shard_splits(T, H, K, dcp_size, torch.cuda.get_device_properties(dev).multi_processor_count)
+            self.num_splits = num_splits
         need = B.sparse_mla_decode_workspace_size(T, H, K, num_splits)
         self.workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev) if need else None
 
@@ -93,6 +96,19 @@ class DcpDecodeStep:
         with torch.cuda.graph(graph):
             self.run(q, ids, req, shards)
         return graph
+
+
+def shard_splits(T: int, H: int, K: int, dcp_size: int, cus: int) -> int:
+    """Top-k ranges per row for the decode of one DCP shard.  The library's automatic plan splits
+    rows that are too few to cover the CUs, keeping at least 256 list entries per range; a shard
+    row holds only about K / dcp_size valid entries (the others are -1), so the same rule is
+    applied to that count.  A range never exceeds the 4096 entries one workgroup compacts, and a
+    call takes at most 64 ranges."""
+    items = T * -(-H // 64)
+    splits = 1
+    if 0 < items < cus:
+        splits = min(-(-cus // items), max(1, -(-K // dcp_size) // 256))
+    return min(max(splits, -(-K // 4096), 1), 64)
 
 
 def device_shards(workload, device="cuda") -> List[Tuple[torch.Tensor, torch.Tensor]]:

@@ -54,3 +54,16 @@ def test_more_than_one_gpu_is_refused():
                        timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_shard_split_plan():
+    # DCP shard decodes are planned for their ~K / D valid entries: c2's DCP4 shards (T = 36,
+    # H = 64, K = 2048) take 2 ranges of >= 256 valid entries instead of 8 ranges of ~64; rows
+    # that already cover the CUs, and long lists, follow the library's own rule
+    from sparse_mla_decode_topk_amd.pipeline import shard_splits
+    assert shard_splits(36, 64, 2048, 4, 256) == 2
+    assert shard_splits(32, 64, 2048, 2, 256) == 4
+    assert shard_splits(256, 128, 2048, 2, 256) == 1
+    assert shard_splits(4224, 128, 2048, 8, 256) == 1
+    assert shard_splits(1, 16, 262144, 2, 256) == 64
+    assert shard_splits(4, 64, 100, 4, 256) == 1

@@ -7,7 +7,7 @@ import torch
 import oracle.smla_oracle as O
 import sparse_mla_decode_topk_amd as smla
 from sparse_mla_decode_topk_amd.pipeline import DcpDecodeStep, device_shards
-from tests.gpu_common import check_close, dev, oracle_unsharded, q_dev, require_gpu
+from tests.gpu_common import OUT_TOL, check_close, dev, oracle_unsharded, q_dev, require_gpu
 from workload import make_config, make_random
 
 pytestmark = pytest.mark.gpu
@@ -84,7 +84,8 @@ def test_dcp4_c2_counts_change_nothing():
     vc = step.valid.cpu().numpy()
     assert np.all(vc[2:, 32:] == 0) and np.all(vc[:2, 32:] == 1)
     for r, (cache, bt) in enumerate(shards):
-        o, l = smla.decode(q_dev(w), cache, step.slots[r], w.sm_scale, out_dtype=torch.float32)
+        o, l = smla.decode(q_dev(w), cache, step.slots[r], w.sm_scale, out_dtype=torch.float32,
+                           num_splits=step.num_splits)
         torch.cuda.synchronize()
         assert torch.equal(o, step.parts[r]) and torch.equal(l, step.lse_parts[r])
 
@@ -117,13 +118,20 @@ def test_dcp8_c4_subset_rows_full_caches():
     print(f"  max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
 
 
+# bf16 shard partials add a third bf16 rounding (P', the partial row, the output) of values up to
+# |out| ~ 4, where half a bf16 ulp is 0.0078: on the c4 rows they measure up to 0.024 from the
+# oracle, past the 2e-2 bar, so they are an opt-in variant checked against this looser bound and
+# the default partials stay fp32.
+BF16_PARTIAL_OUT_TOL = 3e-2
+
+
 @pytest.mark.parametrize("partials", [torch.float32, torch.bfloat16])
 def test_dcp8_c4_full_size_rows(partials):
     """The mixed batch at its full size (T = 4224, 8 shards), in the launch the c4 bench line times,
     against the oracle on every decode row, every prefill row at positions 0-63 (a row at position p
     has p + 1 candidates, so up to 7 of its 8 shards own none and must drop out of the merge) and a
-    sample further along both prompts; with fp32 shard partials (the default) and with bf16 ones
-    (one more rounding of every partial row before the merge)."""
+    sample further along both prompts; with fp32 shard partials (the default, at the 2e-2 bar) and
+    with bf16 ones (one more rounding of every partial row before the merge; BF16_PARTIAL_OUT_TOL)."""
     w = make_config(4)
     print(f"c4 full: T={w.T} H={w.H} D={w.dcp_size} partials {partials}", flush=True)
     step, out, lse = run_step(w, lse_layout="HT", partial_dtype=partials)
@@ -134,7 +142,8 @@ def test_dcp8_c4_full_size_rows(partials):
     assert len(decode_rows) == 128 and len(short) == 128
     rows = sorted(set(decode_rows) | set(short) | set(range(0, w.T, 37)) | {w.T - 1})
     ref_o, ref_l = oracle_unsharded(w, rows)
-    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, what="c4 rows")
+    tol = OUT_TOL if partials == torch.float32 else BF16_PARTIAL_OUT_TOL
+    do, dl = check_close(out[rows], lse[rows], ref_o, ref_l, out_tol=tol, what=f"c4 rows, {partials} partials")
     print(f"  {len(rows)} rows max|dout|={do:.2e} max|dlse|={dl:.2e}", flush=True)
 
 
