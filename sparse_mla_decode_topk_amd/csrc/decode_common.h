@@ -107,9 +107,20 @@ __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
 // read.  Unsplit, the workgroup writes out = 0 and lse = -inf for the block's heads; split, it
 // does nothing (the split merge writes the row).  Returns true when the workgroup is done.
 template <int NT>
+__device__ __forceinline__ void write_marked_empty(const DecodeParams& p, const Block& bk, int tid);
+
+template <int NT>
 __device__ __forceinline__ bool skip_marked_empty(const DecodeParams& p, const Block& bk, int tid) {
   if (p.valid == nullptr || p.valid[bk.row] > 0) return false;
-  if (p.splits > 1) return true;
+  write_marked_empty<NT>(p, bk, tid);
+  return true;
+}
+
+// The output of a row marked empty: out = 0 and lse = -inf for the block's heads when the call
+// has one split (with several, the split merge writes the row).
+template <int NT>
+__device__ __forceinline__ void write_marked_empty(const DecodeParams& p, const Block& bk, int tid) {
+  if (p.splits > 1) return;
   const int per_row = p.out_fp32 ? 4 * kLatent / 16 : 2 * kLatent / 16;  // 16-byte pieces of one head
   for (int c = tid; c < bk.nh * per_row; c += NT) {
     const int h = bk.h_lo + c / per_row, col = c % per_row;
@@ -118,7 +129,6 @@ __device__ __forceinline__ bool skip_marked_empty(const DecodeParams& p, const B
     *reinterpret_cast<i32x4*>(row + 16 * col) = i32x4{0, 0, 0, 0};
   }
   if (tid < bk.nh) p.lse[(int64_t)bk.row * p.l_st + (int64_t)(bk.h_lo + tid) * p.l_sh] = -INFINITY;
-  return true;
 }
 
 // Probability tiles are [token][head] rows of 64 bf16 values (128 bytes) in 8-byte segments of
@@ -225,23 +235,37 @@ __device__ __forceinline__ void store_rows(const DecodeParams& p, const Block& b
   }
 }
 
-// Compacts this split's slot entries that lie in [0, num_slots) into sh.clist, in a fixed
-// order (attention sums over the set); returns their number.  No front-pack is needed upstream.  Every thread loads all of its
-// entries first (at most kMaxEntriesPerSplit / NT), so the list costs one memory round trip;
-// then groups of 4 * NT entries are placed in order, two barriers per group.
-template <class SH, int NT = kThreads>
-__device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block& bk, SH& sh, int tid, int wave,
-                                             int lane) {
-  constexpr int kPer = ((kMaxEntriesPerSplit + NT - 1) / NT + 3) / 4 * 4;  // groups of four per thread
+// This split's slot entries, as loaded by one thread before compaction: at most
+// kMaxEntriesPerSplit / NT of them, in groups of four; -1 past the split's end.
+template <int NT>
+struct SlotEntries {
+  static constexpr int kPer = ((kMaxEntriesPerSplit + NT - 1) / NT + 3) / 4 * 4;
+  int v[kPer];
+};
+
+// Issues every load of this thread's slot entries (the whole list costs one memory round trip).
+template <int NT>
+__device__ __forceinline__ void load_slot_entries(const DecodeParams& p, const Block& bk, int tid,
+                                                  SlotEntries<NT>& se) {
   const int e0 = bk.split * p.entries_per_split;
   const int e1 = min(p.K, e0 + p.entries_per_split);
   const int32_t* srow = p.slots + (int64_t)bk.row * p.slots_ld;
-  int vals[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < SlotEntries<NT>::kPer; ++i) {
     const int e = e0 + i * NT + tid;
-    vals[i] = e < e1 ? srow[e] : -1;
+    se.v[i] = e < e1 ? srow[e] : -1;
   }
+}
+
+// Compacts the loaded entries that lie in [0, num_slots) into sh.clist, in a fixed order
+// (attention sums over the set); returns their number.  No front-pack is needed upstream.
+// Groups of 4 * NT entries are placed in order, two barriers per group.
+template <class SH, int NT>
+__device__ __forceinline__ int compact_loaded(const DecodeParams& p, const Block& bk, SH& sh, int wave, int lane,
+                                              SlotEntries<NT>& se) {
+  constexpr int kPer = SlotEntries<NT>::kPer;
+  const int e0 = bk.split * p.entries_per_split;
+  const int e1 = min(p.K, e0 + p.entries_per_split);
   int total = 0;
 #pragma unroll
   for (int grp = 0; grp < kPer / 4; ++grp) {
@@ -249,8 +273,8 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
     int wcount = 0;
 #pragma unroll
     for (int i = 4 * grp; i < 4 * grp + 4; ++i) {
-      const bool ok = vals[i] >= 0 && (int64_t)vals[i] < p.num_slots;
-      vals[i] = ok ? vals[i] : -1;
+      const bool ok = se.v[i] >= 0 && (int64_t)se.v[i] < p.num_slots;
+      se.v[i] = ok ? se.v[i] : -1;
       wcount += __popcll(__ballot(ok));
     }
     if (lane == 0) sh.wave_cnt[wave] = wcount;
@@ -265,15 +289,24 @@ __device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block&
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 4 * grp; i < 4 * grp + 4; ++i) {
-      const bool ok = vals[i] >= 0;
+      const bool ok = se.v[i] >= 0;
       const unsigned long long bm = __ballot(ok);
-      if (ok) sh.clist[off + __popcll(bm & below)] = vals[i];
+      if (ok) sh.clist[off + __popcll(bm & below)] = se.v[i];
       off += __popcll(bm);
     }
     total += all;
     __syncthreads();
   }
   return total;
+}
+
+// Loads and compacts this split's slot entries (see load_slot_entries and compact_loaded).
+template <class SH, int NT = kThreads>
+__device__ __forceinline__ int compact_slots(const DecodeParams& p, const Block& bk, SH& sh, int tid, int wave,
+                                             int lane) {
+  SlotEntries<NT> se;
+  load_slot_entries<NT>(p, bk, tid, se);
+  return compact_loaded<SH, NT>(p, bk, sh, wave, lane, se);
 }
 
 }  // namespace dec

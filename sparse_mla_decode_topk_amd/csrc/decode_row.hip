@@ -372,12 +372,10 @@ __device__ __forceinline__ void store_staged(const DecodeParams& p, const Block&
 //   per pass: the "over" vote; after a vote for a second pass: two exchange barriers.
 //   Then E (sums published) and the output staging rounds.
 
-template <bool kFull>
-__device__ __forceinline__ void score_role(const DecodeParams& p, const Block& bk, RowShared& sh, int s, int lane) {
+__device__ __forceinline__ void score_role(const DecodeParams& p, const Block& bk, RowShared& sh, int s, int lane,
+                                           const QOps& q) {
   const int G = lane >> 4, r = lane & 15;
   const int tb = s & 1, hh = s >> 1;
-  QOps q;
-  load_q_row<kFull>(p, bk.row, bk.h_lo + 32 * hh + r, G, q);
   const float cq = p.scale_log2;
   SoftmaxState st;
   st.m_ref[0] = st.m_ref[1] = -INFINITY;
@@ -567,11 +565,33 @@ __global__ __launch_bounds__(kRT, 1) void decode_row_kernel(DecodeParams p) {
   const int lane = tid & 63;
 
   Block bk;
-  if (!block_of<kRH>(p, bk) || skip_marked_empty<kRT>(p, bk, tid)) return;
-  bk.total = compact_slots<RowShared, kRT>(p, bk, sh, tid, w, lane);
-  bk.ntiles = (bk.total + kTT - 1) / kTT;
-  if (w < 4) score_role<kFull>(p, bk, sh, w, lane);
-  else value_role(p, bk, sh, w - 4, lane);
+  if (!block_of<kRH>(p, bk)) return;
+  // The row's valid count, its slot entries and (score waves) its q are all requested before any
+  // of them is used, so the prologue costs one memory round trip.  A row counted empty reads
+  // neither further.
+  // (Each role runs its own copy of the compaction, so q is live only in the score waves' code.)
+  const int counted = p.valid != nullptr ? p.valid[bk.row] : 1;
+  SlotEntries<kRT> se;
+  load_slot_entries<kRT>(p, bk, tid, se);
+  if (w < 4) {
+    QOps q;
+    load_q_row<kFull>(p, bk.row, bk.h_lo + 32 * (w >> 1) + (lane & 15), lane >> 4, q);
+    if (counted <= 0) {
+      write_marked_empty<kRT>(p, bk, tid);
+      return;
+    }
+    bk.total = compact_loaded<RowShared, kRT>(p, bk, sh, w, lane, se);
+    bk.ntiles = (bk.total + kTT - 1) / kTT;
+    score_role(p, bk, sh, w, lane, q);
+  } else {
+    if (counted <= 0) {
+      write_marked_empty<kRT>(p, bk, tid);
+      return;
+    }
+    bk.total = compact_loaded<RowShared, kRT>(p, bk, sh, w, lane, se);
+    bk.ntiles = (bk.total + kTT - 1) / kTT;
+    value_role(p, bk, sh, w - 4, lane);
+  }
 }
 
 }  // namespace
