@@ -72,7 +72,7 @@ static_assert(32 * kStg32 <= kStages * kTileBytes && 64 * kStg16 <= kStages * kT
 
 struct RowShared {
   uint8_t stage[kStages * kTileBytes];
-  uint8_t pbuf[2 * kPBuf];  // [buffer][head][token] fp32, 16-byte chunks swizzled by head
+  uint8_t pbuf[2 * kPBuf];  // [buffer][head][token] fp32; chunk c of head row h at c ^ ((h >> 1) & 7)
   int32_t clist[kMaxEntriesPerSplit];
   float xch[2][kRH];  // per token half: the block's per-head maxima or sums, exchanged between halves
   int32_t wave_cnt[kRT / 64];
@@ -236,7 +236,7 @@ __device__ __forceinline__ void softmax_tile(const Scores& S, int tb, int hh, in
       st.l_run[hb] += t[i];
     }
     const int row = 32 * hh + 16 * hb + r;
-    *reinterpret_cast<f32x4*>(pn + row * kPRow + 16 * ((4 * tb + G) ^ (row & 7))) = t;
+    *reinterpret_cast<f32x4*>(pn + row * kPRow + 16 * ((4 * tb + G) ^ ((row >> 1) & 7))) = t;
   }
 }
 
@@ -278,8 +278,8 @@ __device__ __forceinline__ void value_tile(const uint8_t* tile, const uint8_t* p
   auto pread = [&](int ci, f32x4& p0, f32x4& p1) {  // tokens 16ks + 8g + 0..7 of head 32hb + r32
     const int ks = ci >> 1, row = 32 * (ci & 1) + r32;
     const uint8_t* pr = pb + row * kPRow;
-    p0 = *reinterpret_cast<const f32x4*>(pr + 16 * ((4 * ks + 2 * g) ^ (row & 7)));
-    p1 = *reinterpret_cast<const f32x4*>(pr + 16 * ((4 * ks + 2 * g + 1) ^ (row & 7)));
+    p0 = *reinterpret_cast<const f32x4*>(pr + 16 * ((4 * ks + 2 * g) ^ ((row >> 1) & 7)));
+    p1 = *reinterpret_cast<const f32x4*>(pr + 16 * ((4 * ks + 2 * g + 1) ^ ((row >> 1) & 7)));
   };
   auto sread = [&](int ks, f32x4& s0, f32x4& s1) {  // scales of tile v for tokens 16ks + 8g + 0..7
     const int x = (16 * ks + 8 * g) ^ (8 * (v & 1));
