@@ -138,9 +138,9 @@ __device__ __forceinline__ int copy_slot(const RowShared& sh, int n, int total, 
 // Score side
 
 // q of a score lane as B operands of the score MFMAs: head block hb (heads 32hh + 16hb + r of the
-// block), lane group G = lane >> 4.  Latent k-step j (dims 32j .. 32j + 31): lat[hb][j] = dims
-// 32j + 8G + 0..7; rope k-step u: rope[hb][u] = rope dims 32u + 8G + 0..7.  The record operand
-// puts the same dims in the same k-slots.
+// block), lane group G = lane >> 4.  Latent k-steps 2p and 2p + 1 together take dims 64p .. 64p + 63:
+// lat[hb][2p + h] = dims 64p + 16G + 8h + 0..7; rope k-step u: rope[hb][u] = rope dims 32u + 8G +
+// 0..7.  The record operand puts the same dims in the same k-slots.
 struct QOps {
   bf16x8 lat[2][16];
   bf16x8 rope[2][2];
@@ -157,11 +157,11 @@ __device__ __forceinline__ void load_q_row(const DecodeParams& p, int row, int h
       q.rope[hb][0] = q.rope[hb][1] = bf16x8{};
       continue;
     }
-    const uint16_t* qp = p.q + (int64_t)row * p.q_st + (int64_t)h * p.q_sh + 8 * G;
+    const uint16_t* qp = p.q + (int64_t)row * p.q_st + (int64_t)h * p.q_sh;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q.lat[hb][j] = *reinterpret_cast<const bf16x8*>(qp + 32 * j);
-    q.rope[hb][0] = *reinterpret_cast<const bf16x8*>(qp + kLatent);
-    q.rope[hb][1] = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32);
+    for (int j = 0; j < 16; ++j) q.lat[hb][j] = *reinterpret_cast<const bf16x8*>(qp + 64 * (j >> 1) + 16 * G + 8 * (j & 1));
+    q.rope[hb][0] = *reinterpret_cast<const bf16x8*>(qp + kLatent + 8 * G);
+    q.rope[hb][1] = *reinterpret_cast<const bf16x8*>(qp + kLatent + 32 + 8 * G);
   }
 }
 
@@ -171,28 +171,29 @@ struct Scores {
   f32x4 s[2];
 };
 
-// Latent k-step j's record operand for token tok = 16tb + r is bytes 8(G & 1) .. + 7 of chunk
-// 2j + (G >> 1) (dims 32j + 8G .. + 7), one ds_read_b64 at kb + 2j kCS; it is read four k-steps
-// ahead and widened in the k-step before its MFMAs.  Rope k-step u reads rope chunk 4u + G (chunk
-// row 32 + 4u + G).  Tile t's partial scores (k-steps 4t .. 4t + 3) are scaled and added during
-// k-steps 4t + 5 .. 4t + 7, and after the loop for the last tile.
+// The record operands of latent k-steps 2p and 2p + 1 for token tok = 16tb + r are the two halves
+// of chunk 4p + G (dims 64p + 16G .. + 15), one ds_read_b128 at kb + 4p kCS, so that a quarter-wave
+// reads 16 whole chunks of one chunk row; each pair is read three pairs ahead and each half widened
+// in the k-step before its MFMAs.  Rope k-step u reads rope chunk 4u + G (chunk row 32 + 4u + G).
+// Tile t's partial scores (k-steps 4t .. 4t + 3) are scaled and added during k-steps 4t + 5 ..
+// 4t + 7, and after the loop for the last tile.
 __device__ __forceinline__ Scores score_tile(const uint8_t* tile, const QOps& q, int tb, int G, int r) {
   const int tok = 16 * tb + r;
-  const uint8_t* kb = tile + (G >> 1) * kCS + 16 * (tok ^ (8 * (G >> 1))) + 8 * (G & 1);
+  const uint8_t* kb = tile + G * kCS + 16 * (tok ^ (8 * (G & 1)));
   const uint8_t* rb = tile + (32 + G) * kCS + 16 * (tok ^ (8 * (G & 1)));
   const float* srow = reinterpret_cast<const float*>(tile + kScaleBase);
   const int sx = 16 * tb + 4 * G;  // first of this lane's four score tokens
   Scores S;
-  i32x2 kr[16];
+  i32x4 kr[8];
   const bf16x8 ra0 = *reinterpret_cast<const bf16x8*>(rb);
   const bf16x8 ra1 = *reinterpret_cast<const bf16x8*>(rb + 4 * kCS);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kr[j] = *reinterpret_cast<const i32x2*>(kb + 2 * j * kCS);
+  for (int p = 0; p < 3; ++p) kr[p] = *reinterpret_cast<const i32x4*>(kb + 4 * p * kCS);
   S.s[0] = mfma16_bf16(ra0, q.rope[0][0], f32x4{});
   S.s[1] = mfma16_bf16(ra0, q.rope[1][0], f32x4{});
   S.s[0] = mfma16_bf16(ra1, q.rope[0][1], S.s[0]);
   S.s[1] = mfma16_bf16(ra1, q.rope[1][1], S.s[1]);
-  bf16x8 wa = widen8((uint32_t)kr[0][0], (uint32_t)kr[0][1]);
+  bf16x8 wa = widen8((uint32_t)kr[0][0], (uint32_t)kr[0][1]);  // k-step 0: first half of pair 0
   f32x4 acc[2][2];  // partial scores: [tile parity][head block]
   f32x4 sc = {};
 #pragma unroll
@@ -200,8 +201,11 @@ __device__ __forceinline__ Scores score_tile(const uint8_t* tile, const QOps& q,
     const int t = j >> 2, ph = t & 1, tp = t - 1;
     acc[ph][0] = mfma16_bf16(wa, q.lat[0][j], (j & 3) == 0 ? f32x4{} : acc[ph][0]);
     acc[ph][1] = mfma16_bf16(wa, q.lat[1][j], (j & 3) == 0 ? f32x4{} : acc[ph][1]);
-    if (j + 1 < 16) wa = widen8((uint32_t)kr[j + 1][0], (uint32_t)kr[j + 1][1]);
-    if (j + 4 < 16) kr[j + 4] = *reinterpret_cast<const i32x2*>(kb + 2 * (j + 4) * kCS);
+    if (j + 1 < 16) {
+      const i32x4& n = kr[(j + 1) >> 1];
+      wa = (j + 1) & 1 ? widen8((uint32_t)n[2], (uint32_t)n[3]) : widen8((uint32_t)n[0], (uint32_t)n[1]);
+    }
+    if ((j & 1) && j / 2 + 3 < 8) kr[j / 2 + 3] = *reinterpret_cast<const i32x4*>(kb + 4 * (j / 2 + 3) * kCS);
     if (t >= 1 && (j & 3) == 1) sc = *reinterpret_cast<const f32x4*>(srow + kTT * tp + (sx ^ (8 * (tp & 1))));
     if (t >= 1 && (j & 3) >= 2) {  // scores += scale(token, t - 1) * partial of tile t - 1
       const int hb = (j & 3) - 2;
