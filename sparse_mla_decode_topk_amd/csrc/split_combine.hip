@@ -15,7 +15,8 @@
 //
 // One wave per (row, head): lane s < splits reads split s's (m, l), the wave reduces them to
 // M and L and keeps split s's weight 2^(m_s - M) / L in lane s; then every lane owns 8 of the
-// 512 dims and adds the splits' partial rows, eight splits' loads in flight at a time.  A
+// 512 dims and adds the splits' partial rows, eight splits' loads in flight at a time (the first
+// eight issued beside the (max, sum) loads).  A
 // separate kernel rather than an in-kernel "last split to arrive" merge: the kernel boundary
 // publishes the partials to every XCD without a device-scope release and acquire in each
 // workgroup (each of which writes back and invalidates the L2 of its XCD), and the merge
@@ -57,6 +58,19 @@ __global__ __launch_bounds__(64 * kWaves) void split_combine_kernel(DecodeParams
   if (row >= p.T || h >= p.H) return;  // wave-uniform
   const bool marked_empty = p.valid != nullptr && p.valid[row] <= 0;
 
+  // The first eight splits' partial rows are requested together with the (max, sum) pairs (one
+  // memory round trip for both); a split whose weight turns out zero is skipped when adding, so
+  // rows never written by this call (a row marked empty) are read but never used.
+  const f32x4* base = reinterpret_cast<const f32x4*>(p.ws_o + ((int64_t)row * p.splits * p.H + h) * kLatent) + 2 * lane;
+  const int64_t sstride = (int64_t)p.H * kLatent / 4;  // one split further, in 16-byte units
+  f32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < p.splits) {
+      a[i] = __builtin_nontemporal_load(base + i * sstride);
+      b[i] = __builtin_nontemporal_load(base + i * sstride + 1);
+    }
+  }
   float m = -INFINITY, l = 0.0f;
   if (!marked_empty && lane < p.splits) {
     const float* ml = p.ws_ml + (((int64_t)row * p.splits + lane) * p.H + h) * 2;
@@ -71,12 +85,9 @@ __global__ __launch_bounds__(64 * kWaves) void split_combine_kernel(DecodeParams
   if (lane == 0) p.lse[(int64_t)row * p.l_st + (int64_t)h * p.l_sh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2f;
 
   f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  if (!empty) {
-    const f32x4* base = reinterpret_cast<const f32x4*>(p.ws_o + ((int64_t)row * p.splits * p.H + h) * kLatent) + 2 * lane;
-    const int64_t sstride = (int64_t)p.H * kLatent / 4;  // one split further, in 16-byte units
 #pragma unroll 1
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      f32x4 a[8], b[8];
+  for (int s0 = 0; s0 < p.splits; s0 += 8) {
+    if (s0 > 0) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (s0 + i < p.splits) {
@@ -84,14 +95,14 @@ __global__ __launch_bounds__(64 * kWaves) void split_combine_kernel(DecodeParams
           b[i] = __builtin_nontemporal_load(base + (s0 + i) * sstride + 1);
         }
       }
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (s0 + i < p.splits) {
-          const float ws = lane_value(w, s0 + i);
-          if (ws != 0.0f) {  // a zero-weight split adds nothing (and its row may hold no finite values)
-            acc0 += ws * a[i];
-            acc1 += ws * b[i];
-          }
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i < p.splits) {
+        const float ws = lane_value(w, s0 + i);
+        if (ws != 0.0f) {  // a zero-weight split adds nothing (and its row may hold no finite values)
+          acc0 += ws * a[i];
+          acc1 += ws * b[i];
         }
       }
     }
