@@ -310,8 +310,11 @@ def cpu_baseline(w, budget_s, order=None, what=None):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "a5d49d7ba7b4d1c7b63335d8cbdd7e55b3ff5cef3a5d8873848efa7602791230",
-                  "fetch_bytes": 227251920, "write_bytes": 67315648}
+DECODE_TRAFFIC = {"sources_sha256": "6a8dad965ac0eb67a99b9245b8dfc99fc0afd615c62b94e99a6636c16a67a26b",
+                  "fetch_bytes": 227200952, "write_bytes": 67294485}
+# SQ counters of the same shard decode (profiles/decode_row_kernel_c3_dcp2_counters.md): MFMA busy =
+# SQ_VALU_MFMA_BUSY_CYCLES per SIMD over busy cycles, LDS busy = SQ_LDS_IDX_ACTIVE per CU over busy cycles
+DECODE_COUNTERS = {"sources_sha256": "6a8dad965ac0eb67a99b9245b8dfc99fc0afd615c62b94e99a6636c16a67a26b", "mfma_busy": 0.3032, "lds_busy": 0.2319}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode_row.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
@@ -330,6 +333,16 @@ def measured_traffic():
     if t["sources_sha256"] is None or t["sources_sha256"] != kernel_sources_sha256():
         return None
     return int(t["fetch_bytes"] + t["write_bytes"])
+
+
+def measured_counters():
+    """MFMA and LDS busy fractions of the shard decode from the committed counter profile, or None
+    once the kernel sources differ from the ones profiled."""
+    c = DECODE_COUNTERS
+    if c["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return {"mfma_busy": c["mfma_busy"], "lds_busy": c["lds_busy"],
+            "source": "profiles/decode_row_kernel_c3_dcp2_counters.md (rocprofv3 SQ counters)"}
 
 
 def graph_steps(step, q, ids, req, replicas, steps, warmup):
@@ -660,6 +673,9 @@ def main():
     byts, flops = decode_algorithmic(w.T, w.H, w.K, nv_mean, float(np.mean(shard_unique)), out_bytes=4)
     roof = roofline_entry(byts, flops, mean_dec_s)
     roof["traffic"] = measured_traffic()
+    roof["counters"] = measured_counters()
+    if roof["counters"] is not None:
+        roof["mfma_busy"] = roof["counters"]["mfma_busy"]
     roof["kernel"] = "decode_row_kernel (one DCP2 shard call: T=256, H=128, K=2048, ~1024 valid ids/row, fp32 partials)"
     roof["launch_us"] = round(mean_dec_s * 1e6, 2)
     roof["launch_us_p10_p50_p90"] = percentiles_us(dec_ms)

@@ -67,3 +67,13 @@ def test_shard_split_plan():
     assert shard_splits(4224, 128, 2048, 8, 256) == 1
     assert shard_splits(1, 16, 262144, 2, 256) == 64
     assert shard_splits(4, 64, 100, 4, 256) == 1
+
+
+def test_counter_figures_follow_the_kernel_sources(monkeypatch):
+    # the traffic and counter figures belong to the kernel sources they were measured on
+    import bench
+    monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: bench.DECODE_COUNTERS["sources_sha256"])
+    c = bench.measured_counters()
+    assert c is not None and 0.0 < c["mfma_busy"] < 1.0 and 0.0 < c["lds_busy"] < 1.0
+    monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: "0" * 64)
+    assert bench.measured_counters() is None and bench.measured_traffic() is None
