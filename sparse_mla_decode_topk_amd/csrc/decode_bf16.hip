@@ -308,8 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeParams p
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
-  const int64_t items = (int64_t)p.T * plan.head_blocks * plan.splits;
-  const unsigned grid = (unsigned)((items + 7) / 8 * 8);
+  const unsigned grid = (unsigned)decode_grid(p.T, plan.head_blocks, plan.splits);
   hipLaunchKernelGGL(decode_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;

@@ -85,17 +85,21 @@ struct Block {
   int row, hb, split, h_lo, nh, total, ntiles;
 };
 
-// Work item of this workgroup: (row, head block of HB heads, split), or false past the last one.
-// Consecutive blocks are dispatched round-robin over the 8 XCDs; every XCD gets a contiguous
-// range of work items, so the head blocks and splits of a row, and neighbouring rows (the MTP
-// rows of a request share records), run side by side on one XCD and share its L2.
+// Work item of this workgroup: (row, head block of HB heads, split), or false when the grid slot
+// holds none.  Rows go to the 8 XCDs in groups of kRowGroup consecutive rows, group g to XCD
+// g % 8 (workgroup b runs on XCD b % 8), so the items of a group (every head block and split of
+// its rows: the MTP rows of a request share records) run side by side on one XCD and share its
+// L2, while rows whose work grows or shrinks along the batch (prefill rows at increasing
+// positions) spread evenly over the XCDs.  The grid is decode_grid() slots.
 template <int HB = kHB>
 __device__ __forceinline__ bool block_of(const DecodeParams& p, Block& bk) {
-  const int per_xcd = (int)((gridDim.x + 7) / 8);
-  const int wg = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (wg >= p.T * p.head_blocks * p.splits) return false;
-  bk.split = wg % p.splits;
-  const int rest = wg / p.splits;
+  const int per_group = kRowGroup * p.head_blocks * p.splits;
+  const int k = (int)(blockIdx.x / 8);
+  const int group = (int)(blockIdx.x % 8) + 8 * (k / per_group);
+  const int64_t wg = (int64_t)group * per_group + k % per_group;
+  if (wg >= (int64_t)p.T * p.head_blocks * p.splits) return false;
+  bk.split = (int)(wg % p.splits);
+  const int rest = (int)(wg / p.splits);
   bk.hb = rest % p.head_blocks;
   bk.row = rest / p.head_blocks;
   bk.h_lo = bk.hb * HB;

@@ -601,8 +601,7 @@ __global__ __launch_bounds__(kRT, 1) void decode_row_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode_row(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
-  const int64_t items = (int64_t)p.T * plan.head_blocks * plan.splits;
-  const unsigned grid = (unsigned)((items + 7) / 8 * 8);
+  const unsigned grid = (unsigned)decode_grid(p.T, plan.head_blocks, plan.splits);
   if (p.H % kRH == 0)
     hipLaunchKernelGGL(decode_row_kernel<true>, dim3(grid), dim3(kRT), 0, stream, p);
   else

@@ -159,7 +159,7 @@ int prepare_decode(const void* q, int64_t q_stride_t, int64_t q_stride_h, const 
   const int cus = num_splits > 0 ? 256 : device_cus();
   plan = make_plan(T, H, K, num_splits, cus, hpb);
   if ((int64_t)K > (int64_t)plan.splits * kMaxEntriesPerSplit) return SMLA_ERR_UNSUPPORTED;
-  if ((int64_t)T * plan.head_blocks * plan.splits > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
+  if (decode_grid(T, plan.head_blocks, plan.splits) > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
   if (plan.ws_total > 0) {
     if (!workspace || workspace_bytes < plan.ws_total) return SMLA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SMLA_ERR_MISALIGNED;

@@ -16,6 +16,15 @@ constexpr int kMaxEntriesPerSplit = 4096;  // slot entries one decode workgroup 
 constexpr int kMaxSplits = 64;
 constexpr int kHeadsPerBlock = 64;           // heads one workgroup of the bf16-record decode covers
 constexpr int kRowHeads = 64;                // heads one workgroup of the fp8_ds_mla decode covers
+constexpr int kRowGroup = 4;                 // consecutive rows whose decode work items share an XCD
+
+// Workgroups of a decode launch: the work items of groups of kRowGroup rows, the groups dealt
+// round-robin to the 8 XCDs (see block_of); slots past the last item stay idle.
+inline int64_t decode_grid(int64_t T, int64_t head_blocks, int64_t splits) {
+  const int64_t per_group = kRowGroup * head_blocks * splits;
+  const int64_t groups = (T + kRowGroup - 1) / kRowGroup;
+  return 8 * ((groups + 7) / 8) * per_group;
+}
 
 struct ConvertParams {
   const int32_t* ids;
