@@ -3,7 +3,7 @@
 // page "FlashMLA sparse fp8 path gains DCP and MTP" contrasts with the packed fp8_ds_mla one
 // ("Related": 576 against 656; "Risks and impact": the bf16 sparse path).  Same contract as
 // the fp8 decode: out[t,h,0:512] and lse[t,h] of softmax attention over the row's own
-// candidate records, (0, -inf) for a row without one, split-K with an in-kernel merge.
+// candidate records, (0, -inf) for a row without one, split-K merged by split_combine.hip.
 //
 // gfx950 design (the fp8 kernel's structure, without scales, query split or widening)
 //  * A workgroup owns one row, up to 64 heads and one range of the row's top-k list: four

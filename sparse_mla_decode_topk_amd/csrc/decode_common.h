@@ -1,6 +1,6 @@
 // Device helpers shared by the decode kernels of both record layouts (fp8_ds_mla and plain
 // bf16): workgroup-to-work mapping, slot-list compaction, LDS-only barriers, HBM -> LDS
-// copies, MFMA wrappers and the split-K arrival and merge.  Each kernel keeps its own tile
+// copies, MFMA wrappers and output staging.  Each kernel keeps its own tile
 // layout, roles and main loop.
 
 #pragma once

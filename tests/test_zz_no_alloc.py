@@ -1,8 +1,8 @@
 """The decode entry point that allocates nothing (sparse_mla_decode_noalloc) against the
 workspace entry point (sparse_mla_decode): same kernels and split plan, so the results must be
 bitwise equal.  Two calls in a row, the second smaller, both with split-K so the scratch array
-carries the partials and the arrival counters; a plan that needs more scratch than the library
-holds is refused before anything is launched."""
+carries the partials and (max, sum) pairs; a plan that needs more scratch than the library holds
+is refused before anything is launched."""
 import pytest
 import torch
 
