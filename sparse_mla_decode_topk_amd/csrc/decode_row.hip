@@ -61,8 +61,8 @@ constexpr int kScaleBase = kChunkRows * kCS;          // record scales [4][32] f
 constexpr int kTileBytes = kScaleBase + 4 * kTT * 4;  // 20992
 constexpr int kStages = 4;                            // tile ring: scores on n, values on n-1,
 constexpr int kAhead = 2;                             //   copies in flight for n+1, n+2
-constexpr int kPRow = 4 * kTT;                        // fp32 probabilities of one head for one tile
-constexpr int kPBuf = kRH * kPRow;                    // 8 KB: the probabilities of one tile
+constexpr int kPRow = 4 * kTT + 16;                   // fp32 probabilities of one head for one tile, padded
+constexpr int kPBuf = kRH * kPRow;                    // 9 KB: the probabilities of one tile
 constexpr int kStg32 = 4 * kLatent + 16;              // staged output rows: fp32 and bf16 pitches
 constexpr int kStg16 = 2 * kLatent + 16;              //   (16 bytes of padding: rows 4 banks apart)
 
@@ -72,7 +72,7 @@ static_assert(32 * kStg32 <= kStages * kTileBytes && 64 * kStg16 <= kStages * kT
 
 struct RowShared {
   uint8_t stage[kStages * kTileBytes];
-  uint8_t pbuf[2 * kPBuf];  // [buffer][head][token] fp32; chunk c of head row h at c ^ ((h >> 1) & 7)
+  uint8_t pbuf[2 * kPBuf];  // [buffer][head][token] fp32, head rows 144 bytes apart
   int32_t clist[kMaxEntriesPerSplit];
   float xch[2][kRH];  // per token half: the block's per-head maxima or sums, exchanged between halves
   int32_t wave_cnt[kRT / 64];
@@ -225,8 +225,10 @@ struct SoftmaxState {
   float m_ref[2], m_raw[2], l_run[2];
 };
 
-// Softmax of this lane's scores (entries at or past `nin` get p = 0) against each head's
-// reference: probabilities to the heads' rows of `pn`, running raw max and sum.
+// Softmax of this lane's scores against each head's reference: probabilities to the heads' rows
+// of `pn`, running raw max and sum.  kMask: entries at or past `nin` get p = 0 (only a range's
+// last tile can hold such entries; the other tiles skip the compare and select).
+template <bool kMask>
 __device__ __forceinline__ void softmax_tile(const Scores& S, int tb, int hh, int G, int r, int nin, float cq,
                                              SoftmaxState& st, uint8_t* pn) {
 #pragma unroll
@@ -234,13 +236,13 @@ __device__ __forceinline__ void softmax_tile(const Scores& S, int tb, int hh, in
     f32x4 t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = 16 * tb + 4 * G + i < nin ? S.s[hb][i] : -INFINITY;
+      const float v = !kMask || 16 * tb + 4 * G + i < nin ? S.s[hb][i] : -INFINITY;
       st.m_raw[hb] = __builtin_elementwise_maximum(st.m_raw[hb], v);
       t[i] = fast_exp2(fmaf(v, cq, -st.m_ref[hb]));
       st.l_run[hb] += t[i];
     }
     const int row = 32 * hh + 16 * hb + r;
-    *reinterpret_cast<f32x4*>(pn + row * kPRow + 16 * ((4 * tb + G) ^ ((row >> 1) & 7))) = t;
+    *reinterpret_cast<f32x4*>(pn + row * kPRow + 16 * (4 * tb + G)) = t;
   }
 }
 
@@ -282,8 +284,8 @@ __device__ __forceinline__ void value_tile(const uint8_t* tile, const uint8_t* p
   auto pread = [&](int ci, f32x4& p0, f32x4& p1) {  // tokens 16ks + 8g + 0..7 of head 32hb + r32
     const int ks = ci >> 1, row = 32 * (ci & 1) + r32;
     const uint8_t* pr = pb + row * kPRow;
-    p0 = *reinterpret_cast<const f32x4*>(pr + 16 * ((4 * ks + 2 * g) ^ ((row >> 1) & 7)));
-    p1 = *reinterpret_cast<const f32x4*>(pr + 16 * ((4 * ks + 2 * g + 1) ^ ((row >> 1) & 7)));
+    p0 = *reinterpret_cast<const f32x4*>(pr + 16 * (4 * ks + 2 * g));
+    p1 = *reinterpret_cast<const f32x4*>(pr + 16 * (4 * ks + 2 * g + 1));
   };
   auto sread = [&](int ks, f32x4& s0, f32x4& s1) {  // scales of tile v for tokens 16ks + 8g + 0..7
     const int x = (16 * ks + 8 * g) ^ (8 * (v & 1));
@@ -406,11 +408,13 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
         for (int hb = 0; hb < 2; ++hb)
           st.m_ref[hb] = __builtin_elementwise_maximum(mx[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) * cq;
       }
-      softmax_tile(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
+      if (bk.ntiles > 1) softmax_tile<false>(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
+      else softmax_tile<true>(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
       for (int n = 1; n < bk.ntiles; ++n) {
         lds_barrier();  // Bn
         const Scores Sn = score_tile(sh.stage + (n % kStages) * kTileBytes, q, tb, G, r);
-        softmax_tile(Sn, tb, hh, G, r, bk.total - n * kTT, cq, st, sh.pbuf + (n & 1) * kPBuf);
+        if (n + 1 < bk.ntiles) softmax_tile<false>(Sn, tb, hh, G, r, kTT, cq, st, sh.pbuf + (n & 1) * kPBuf);
+        else softmax_tile<true>(Sn, tb, hh, G, r, bk.total - n * kTT, cq, st, sh.pbuf + (n & 1) * kPBuf);
       }
       lds_barrier();  // Blast
     }
