@@ -150,7 +150,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       float pv[4];  // raw scores of heads 4g + r; cq > 0 scales them into log2 units below
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = acc0[r] + acc1[r];
-      if (tok >= bk.total - n * kTT) {  // tail tile: entries past the end of the list get p = 0
+      if (n + 1 == bk.ntiles && tok >= bk.total - n * kTT) {  // tail tile: entries past the list end get p = 0
 #pragma unroll
         for (int r = 0; r < 4; ++r) pv[r] = -INFINITY;
       }
