@@ -1,5 +1,6 @@
 // Achievable-peak microbenchmarks for the units the sparse MLA decode relies on, on gfx950:
-// streaming HBM copy and read, dense bf16 and fp8 MFMA chains, the e4m3 -> bf16 widening
+// streaming HBM copy and read, dense bf16 and fp8 MFMA chains (and the latency of dependent
+// ones), the e4m3 -> bf16 widening
 // conversion, and an MFMA stream with independent vector work beside it in the same wave.
 // Built into a library of its own (libsmla_peak.so): measurement, not part of the decode path.
 //
@@ -88,6 +89,31 @@ __global__ __launch_bounds__(512) void k_mfma_bf16(int iters, float* sink) {
                  : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7));
     r = c0[0] + c1[1] + c2[2] + c3[3] + c4[0] + c5[1] + c6[2] + c7[3];
   }
+  if (r == 1234.5f) sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+// C dependent chains of 16x16x32 bf16 MFMAs per wave (C = 1, 2, 4 or 8), each advanced once per
+// iteration: with few chains every MFMA waits for the result of the one before it on its
+// accumulator, so the time per MFMA against C gives the dependent-issue latency.
+template <int C>
+__global__ __launch_bounds__(512) void k_mfma_chain(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  i32x4 ai = {lane, lane + 1, lane + 2, lane + 3};
+  i32x4 bi = {lane * 3, lane ^ 5, 7, lane + 9};
+  ai &= 0x3f803f80;  // small normal bf16 values
+  bi &= 0x3f803f80;
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ai), b = __builtin_bit_cast(bf16x8, bi);
+  f32x4 c[C];
+#pragma unroll
+  for (int k = 0; k < C; ++k) c[k] = f32x4{0.0f, 0.0f, 0.0f, (float)k};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < C; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int k = 0; k < C; ++k) r += c[k][0] + c[k][3];
   if (r == 1234.5f) sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
 
@@ -395,6 +421,20 @@ int smla_peak_mfma(int kind, int iters, int grid, int waves_per_wg, float* sink,
   else if (kind == 1) hipLaunchKernelGGL(k_mfma_bf16<1>, dim3(grid), blk, 0, stream, iters, sink);
   else if (kind == 2) hipLaunchKernelGGL(k_mfma_fp8, dim3(grid), blk, 0, stream, iters, sink);
   else return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// `chains` (1, 2, 4 or 8) dependent 16x16x32 bf16 MFMA chains per wave, `iters` MFMAs each.
+int smla_peak_chain(int chains, int iters, int grid, int waves_per_wg, float* sink, hipStream_t stream) {
+  if (waves_per_wg < 1 || waves_per_wg > 8) return 1;
+  const dim3 blk(64 * waves_per_wg);
+  switch (chains) {
+    case 1: hipLaunchKernelGGL(k_mfma_chain<1>, dim3(grid), blk, 0, stream, iters, sink); break;
+    case 2: hipLaunchKernelGGL(k_mfma_chain<2>, dim3(grid), blk, 0, stream, iters, sink); break;
+    case 4: hipLaunchKernelGGL(k_mfma_chain<4>, dim3(grid), blk, 0, stream, iters, sink); break;
+    case 8: hipLaunchKernelGGL(k_mfma_chain<8>, dim3(grid), blk, 0, stream, iters, sink); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

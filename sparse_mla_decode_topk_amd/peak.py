@@ -1,7 +1,8 @@
 """Achievable-peak microbenchmarks (libsmla_peak.so, built from csrc/peak.hip).
 
 Measures, on the current device, what plain loops reach on the units the decode depends on:
-HBM streaming (copy and read), dense MFMA chains (bf16 32x32x16 and 16x16x32, fp8 32x32x64),
+HBM streaming (copy and read), dense MFMA chains (bf16 32x32x16 and 16x16x32, fp8 32x32x64) and
+the time per MFMA of 1, 2, 4 or 8 dependent 16x16x32 chains per wave,
 the e4m3 -> bf16 widening conversion, and MFMA with independent fp32 FMAs beside it in one
 wave.  Each figure is also given as a fraction of MI355X's published peak (HBM 8 TB/s; dense
 bf16 2.5 PFLOP/s, fp8 5.0 PFLOP/s) so a kernel's roofline fraction can be read against what
@@ -48,8 +49,10 @@ def load():
             lib.smla_peak_valu.argtypes = [_I32, _I32, _I32, _I32, _P, _P]
             lib.smla_peak_lds.argtypes = [_I32, _I32, _I32, _I32, _P, _P]
             lib.smla_peak_dual.argtypes = [_I32, _I32, _I32, _I32, _P, _P]
+            lib.smla_peak_chain.argtypes = [_I32, _I32, _I32, _I32, _P, _P]
             for f in ("smla_peak_copy", "smla_peak_read", "smla_peak_mfma", "smla_peak_mix", "smla_peak_cvt",
-                      "smla_peak_clock", "smla_peak_mixi", "smla_peak_valu", "smla_peak_lds", "smla_peak_dual"):
+                      "smla_peak_clock", "smla_peak_mixi", "smla_peak_valu", "smla_peak_lds", "smla_peak_dual",
+                      "smla_peak_chain"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -124,6 +127,14 @@ def run(mib: int = 1024, iters: int = 4096, cus: int | None = None, quick: bool 
                 ms = _time_ms(lambda: _check(fn(nv, iters, cus, 4 * wps, sink.data_ptr(), _stream()), key))
                 mix[f"w{wps}_nv{nv}"] = round(ms * 1e6 / iters, 2)  # ns per iteration per wave
         res[key] = mix
+
+    # dependent 16x16x32 bf16 MFMA chains: ns per MFMA per SIMD for 1, 2, 4, 8 chains per wave
+    chain = {}
+    for wps in (1, 2):
+        for c in (1, 2, 4, 8):
+            ms = _time_ms(lambda: _check(lib.smla_peak_chain(c, iters, cus, 4 * wps, sink.data_ptr(), _stream()), "chain"))
+            chain[f"w{wps}_chains{c}"] = round(ms * 1e6 / (iters * c * wps), 3)
+    res["mfma16_chain_ns_per_mfma_per_simd"] = chain
 
     # vector issue: ns per instruction per SIMD for 32 independent instances per iteration
     ops = ("v_fma_f32", "v_cvt_scalef32_pk_bf16_fp8", "v_cvt_pk_f32_fp8", "v_perm_b32", "v_exp_f32",
