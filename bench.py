@@ -179,14 +179,19 @@ def main_dense(args):
     if not args.no_cpu_baseline:
         import oracle.smla_oracle as O
         log("timing the CPU oracle on a bounded sample ...")
-        rows_done, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_budget:
+        tally = ParityTally(*host_result(out, lse))
+        rows_done, t0, t_cmp = 0, time.perf_counter(), 0.0
+        while time.perf_counter() - t0 - t_cmp < args.cpu_budget:
             t = rows_done % w.T
             sub = w.rows([t])
             sl, _ = O.convert_index(sub.ids, sub.req, sub.block_table, sub.block_size)
-            O.attention_rows(sub.q_f32(), sl, sub.cache, sub.cache.num_slots, sub.sm_scale)
+            ref = O.attention_rows(sub.q_f32(), sl, sub.cache, sub.cache.num_slots, sub.sm_scale)
             rows_done += 1
-        el = time.perf_counter() - t0
+            tc = time.perf_counter()
+            tally.add([t], *ref)
+            t_cmp += time.perf_counter() - tc
+        el = time.perf_counter() - t0 - t_cmp
+        line["parity"] = tally.result()
         line["cpu_baseline"] = {"value": round(rows_done / el, 3), "unit": "query-rows/s", "cores": blas_threads(),
                                 "kind": "oracle",
                                 "sample": f"{rows_done} rows of the same workload in order through the fp64 numpy "
@@ -252,13 +257,19 @@ def main_bf16(args):
     if not args.no_cpu_baseline:
         import oracle.smla_oracle as O
         log("timing the CPU oracle on a bounded sample ...")
-        rows_done, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_budget:
-            sub = w.rows([rows_done % w.T])
+        tally = ParityTally(*host_result(out, lse))
+        rows_done, t0, t_cmp = 0, time.perf_counter(), 0.0
+        while time.perf_counter() - t0 - t_cmp < args.cpu_budget:
+            t = rows_done % w.T
+            sub = w.rows([t])
             sl, _ = O.convert_index(sub.ids, sub.req, sub.block_table, sub.block_size)
-            O.attention_rows(sub.q_f32(), sl, sub.cache, sub.cache.num_slots, sub.sm_scale, record_layout="bf16")
+            ref = O.attention_rows(sub.q_f32(), sl, sub.cache, sub.cache.num_slots, sub.sm_scale, record_layout="bf16")
             rows_done += 1
-        el = time.perf_counter() - t0
+            tc = time.perf_counter()
+            tally.add([t], *ref)
+            t_cmp += time.perf_counter() - tc
+        el = time.perf_counter() - t0 - t_cmp
+        line["parity"] = tally.result()
         line["cpu_baseline"] = {"value": round(rows_done / el, 3), "unit": "query-rows/s", "cores": blas_threads(),
                                 "kind": "oracle",
                                 "sample": f"{rows_done} rows of the same workload in order through the fp64 numpy "
@@ -267,10 +278,53 @@ def main_bf16(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, budget_s, order=None, what=None):
+def host_result(out, lse):
+    """The step's final (out, lse) copied to host memory as float32 numpy arrays [T,H,512], [T,H]."""
+    return out.float().cpu().numpy(), lse.float().cpu().numpy()
+
+
+class ParityTally:
+    """Distances of GPU results from the oracle's on the rows the oracle computed (each row once)."""
+
+    def __init__(self, gpu_out, gpu_lse):
+        self.out, self.lse = gpu_out, gpu_lse
+        self.seen = set()
+        self.dout = self.dlse = self.max_out = 0.0
+        self.inf_ok = True
+        self.finite = True
+
+    def add(self, rows, ref_o, ref_l):
+        import numpy as np
+        keep = [i for i, r in enumerate(rows) if r not in self.seen]
+        if not keep:
+            return
+        rr = [rows[i] for i in keep]
+        self.seen.update(rr)
+        go, gl = self.out[rr].astype(np.float64), self.lse[rr].astype(np.float64)
+        ro, rl = np.asarray(ref_o)[keep], np.asarray(ref_l)[keep]
+        self.finite &= bool(np.isfinite(go).all()) and not bool(np.isnan(gl).any())
+        self.dout = max(self.dout, float(np.abs(go - ro).max()))
+        self.max_out = max(self.max_out, float(np.abs(ro).max()))
+        fin = np.isfinite(rl)
+        self.inf_ok &= bool(np.array_equal(np.isneginf(gl), np.isneginf(rl)))
+        if fin.any():
+            self.dlse = max(self.dlse, float(np.abs(gl[fin] - rl[fin]).max()))
+
+    def result(self):
+        return {"rows_checked": len(self.seen), "max_abs_dout": self.dout, "max_abs_dlse": self.dlse,
+                "max_abs_out": self.max_out, "out_tolerance": 2e-2, "lse_tolerance": 1e-3,
+                "out_margin": round(2e-2 / self.dout, 2) if self.dout else None,
+                "lse_margin": round(1e-3 / self.dlse, 1) if self.dlse else None,
+                "neg_inf_lse_identical": self.inf_ok, "no_nan": self.finite,
+                "within_tolerance": bool(self.finite and self.inf_ok and self.dout <= 2e-2 and self.dlse <= 1e-3),
+                "against": "the fp64 oracle rows of cpu_baseline, every element of each row"}
+
+
+def cpu_baseline(w, budget_s, order=None, what=None, gpu=None):
     """fp64 oracle of the same DCP step (converts, shard attention, merge) over the rows in
     `order` (default: in order), wrapping around, until the time budget is spent; rows/s over
-    the rows done."""
+    the rows done.  gpu: the step's host (out, lse); the oracle rows are then also compared
+    with it (outside the timed part) and the distances come back under "parity"."""
     import numpy as np
     import oracle.smla_oracle as O
     try:
@@ -279,9 +333,10 @@ def cpu_baseline(w, budget_s, order=None, what=None):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     order = list(range(w.T)) if order is None else [int(r) for r in order]
-    rows_done, t0 = 0, time.perf_counter()
+    tally = ParityTally(*gpu) if gpu is not None else None
+    rows_done, t0, t_cmp = 0, time.perf_counter(), 0.0
     chunk = 4
-    while time.perf_counter() - t0 < budget_s:
+    while time.perf_counter() - t0 - t_cmp < budget_s:
         start = rows_done % len(order)
         rows = order[start:start + chunk]
         sub = w.rows(rows)
@@ -289,22 +344,27 @@ def cpu_baseline(w, budget_s, order=None, what=None):
         outs, lses = [], []
         if sub.dcp_size == 1:  # one cache, no merge
             s, _ = O.convert_index(sub.ids, sub.req, sub.block_table, sub.block_size)
-            O.attention_rows(q, s, sub.cache, sub.cache.num_slots, sub.sm_scale)
+            ref = O.attention_rows(q, s, sub.cache, sub.cache.num_slots, sub.sm_scale)
         else:
             for sh in sub.shards:
                 s, _ = O.convert_index(sub.ids, sub.req, sh.block_table, sub.block_size, sub.dcp_size, sh.rank)
                 o, l = O.attention_rows(q, s, sh.cache, sh.cache.num_slots, sub.sm_scale)
                 outs.append(o)
                 lses.append(l)
-            O.merge_lse(np.stack(outs), np.stack(lses))
+            ref = O.merge_lse(np.stack(outs), np.stack(lses))
         rows_done += len(rows)
-    dt = time.perf_counter() - t0
-    return {"value": round(rows_done / dt, 3), "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
+        if tally is not None:
+            tc = time.perf_counter()
+            tally.add(rows, *ref)
+            t_cmp += time.perf_counter() - tc
+    dt = time.perf_counter() - t0 - t_cmp
+    res = {"value": round(rows_done / dt, 3), "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows_done} rows ({what or f'the {w.T} rows of the same DCP{w.dcp_size} step in order'}, "
                       f"wrapping) through the fp64 numpy oracle: "
                       + ("convert and attention" if w.dcp_size == 1 else
                          f"{w.dcp_size} shard converts, shard attention, LSE merge")
                       + f"; {dt:.1f} s on {os.cpu_count()} host CPUs"}
+    return (res, tally.result()) if tally is not None else res
 
 
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
@@ -458,6 +518,7 @@ def main_small(args, cid):
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t_start
     wall = graph_steps(step, q, ids, req, replicas, args.steps, args.warmup)
+    gpu = None if args.no_cpu_baseline else host_result(step.out, step.lse)  # the last replay's result
     dec_ms = decode_launch_ms(step, q, replicas)
     mean_dec_s = float(np.mean(dec_ms)) / 1e3
     byts, flops = decode_algorithmic(w.T, w.H, w.K, float(np.mean(shard_valid)), float(np.mean(shard_unique)),
@@ -485,7 +546,7 @@ def main_small(args, cid):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(w, args.cpu_budget, gpu=gpu)
     print(json.dumps(line), flush=True)
 
 
@@ -527,6 +588,7 @@ def main_c4(args):
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t_start
     wall = graph_steps(step, q, ids, req, [shards], args.steps, args.warmup)
+    gpu = None if args.no_cpu_baseline else host_result(step.out, step.lse)  # the last replay's result
     dec_ms = decode_launch_ms(step, q, [shards], launches=16, rounds=3)
     mean_dec_s = float(np.mean(dec_ms)) / 1e3
     byts, flops = decode_algorithmic(w.T, w.H, w.K, float(np.mean(shard_valid)), float(np.mean(shard_unique)),
@@ -572,8 +634,8 @@ def main_c4(args):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         order = np.random.Generator(np.random.PCG64(4004)).permutation(w.T)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, order=order,
-                                            what=f"the {w.T} rows of the DCP8 step in a seeded random order")
+        line["cpu_baseline"], line["parity"] = cpu_baseline(
+            w, args.cpu_budget, order=order, what=f"the {w.T} rows of the DCP8 step in a seeded random order", gpu=gpu)
     print(json.dumps(line), flush=True)
 
 
@@ -662,6 +724,7 @@ def main():
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t_start
     wall = graph_steps(step, q, ids, req, replicas, args.steps, args.warmup)
+    gpu = None if args.no_cpu_baseline else host_result(step.out, step.lse)  # the last replay's result
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = w.T * args.steps / wall
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (graph), {eager_wall * 1e3 / args.steps:.4f} (eager)")
@@ -728,7 +791,7 @@ def main():
     line["cache_write"] = cache_write
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(w, args.cpu_budget, gpu=gpu)
     print(json.dumps(line), flush=True)
 
 

@@ -77,3 +77,28 @@ def test_counter_figures_follow_the_kernel_sources(monkeypatch):
     assert c is not None and 0.0 < c["mfma_busy"] < 1.0 and 0.0 < c["lds_busy"] < 1.0
     monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: "0" * 64)
     assert bench.measured_counters() is None and bench.measured_traffic() is None
+
+
+def test_parity_tally_reports_the_largest_distances_once_per_row():
+    """The bench's oracle comparison: each row counts once, the -inf pattern must match, and the
+    largest element distances and the margins to the 2e-2 / 1e-3 bars are what it reports."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    ref_o = rng.standard_normal((6, 4, 512))
+    ref_l = rng.standard_normal((6, 4))
+    ref_o[2], ref_l[2] = 0.0, -np.inf  # an empty row
+    gpu_o = (ref_o + 1e-3).astype(np.float32)
+    gpu_l = ref_l.astype(np.float32)
+    gpu_o[4, 1, 7] += 4e-3  # the largest out distance: 5e-3
+    gpu_l[5, 3] += 2e-4
+    t = bench.ParityTally(gpu_o, gpu_l)
+    t.add([0, 1, 2], ref_o[[0, 1, 2]], ref_l[[0, 1, 2]])
+    t.add([2, 3, 4, 5], ref_o[[2, 3, 4, 5]], ref_l[[2, 3, 4, 5]])  # row 2 again: counted once
+    r = t.result()
+    assert r["rows_checked"] == 6
+    assert abs(r["max_abs_dout"] - 5e-3) < 1e-6 and abs(r["max_abs_dlse"] - 2e-4) < 1e-6
+    assert r["neg_inf_lse_identical"] and r["no_nan"] and r["within_tolerance"]
+    assert abs(r["out_margin"] - 4.0) < 0.01
+    bad = bench.ParityTally(gpu_o, np.where(np.isinf(gpu_l), np.float32(0.0), gpu_l))
+    bad.add([2], ref_o[[2]], ref_l[[2]])  # a finite LSE where the oracle has -inf
+    assert not bad.result()["neg_inf_lse_identical"] and not bad.result()["within_tolerance"]
