@@ -23,17 +23,19 @@
 //    fp32.)  Each 128-dim scale tile is four k-steps; its fp32 record scale then multiplies the
 //    tile's partial scores.  The score wave then runs the softmax of its scores: base 2, against
 //    a per-head reference max fixed at the first tile (the two waves that share a head exchange
-//    their halves of that max through LDS once); later probabilities are 2^(s - ref) and may
-//    exceed 1, which fp32 accumulators hold; should a score exceed the reference by more than
-//    2^64 the workgroup recomputes the range once with the exact max, so the output
-//    accumulators are never rescaled inside the loop.
+//    their halves of that max through LDS once, and the reference also carries 2^e, e the
+//    exponent of the first tile's largest record scale); later probabilities are 2^(s - ref) and
+//    may exceed 2^-e; should a score exceed the reference by more than 2^12, or a product
+//    p * scale overflow fp16 below, the workgroup recomputes the range once with the exact max
+//    and the exponent of the range's largest scale, so the output accumulators are never
+//    rescaled inside the loop.
 //  * Value wave v copies a quarter of every tile HBM -> LDS and produces the output of every
 //    head of the block over the latent dims 128v .. 128v + 127, i.e. over record scale tile v
 //    (128 dims x 64 heads of fp32 accumulators), as O^T = V^T . P'^T on
-//    v_mfma_f32_32x32x16_bf16: V^T fragments come from the staged tile through
-//    ds_read_b64_tr_b8 and are widened exactly to bf16; P' = p * scale(token, v) is rounded once
-//    to bf16 from the fp32 probabilities, which cross from the score waves through LDS,
-//    double-buffered.  Step n scores tile n and outputs tile n - 1; one workgroup barrier per
+//    v_mfma_f32_32x32x16_f16: V^T fragments come from the staged tile through
+//    ds_read_b64_tr_b8 and are widened exactly to fp16; P' = p * scale(token, v) is rounded once
+//    to fp16 (11 significant bits, four times finer than bf16) from the fp32 probabilities,
+//    which cross from the score waves through LDS, double-buffered.  Step n scores tile n and outputs tile n - 1; one workgroup barrier per
 //    step orders that hand-over and the tile ring.
 //  * Gather: the row's slot range is compacted in LDS (-1 and out-of-range entries dropped),
 //    then tiles of 32 records are copied with global_load_lds, two tiles ahead.  A tile sits
@@ -66,6 +68,12 @@ constexpr int kPBuf = kRH * kPRow;                    // 9 KB: the probabilities
 constexpr int kStg32 = 4 * kLatent + 16;              // staged output rows: fp32 and bf16 pitches
 constexpr int kStg16 = 2 * kLatent + 16;              //   (16 bytes of padding: rows 4 banks apart)
 
+// First-pass headroom (log2 units): probabilities stay below 2^12 times the power of two that
+// scales them (see score_role), so p * scale fits fp16 unless a later record's scale is far
+// larger than the first tile's; such a product overflows, the value waves see a non-finite
+// accumulator and the range is repeated with exact references.
+constexpr float kPHeadroom = 12.0f;
+
 static_assert(kRH == 64, "score waves: 2 token halves x 2 head halves of 32; output blocks of 32 heads");
 static_assert(kStages == kAhead + 2, "ring: the tile being scored, the one being valued, the copies");
 static_assert(32 * kStg32 <= kStages * kTileBytes && 64 * kStg16 <= kStages * kTileBytes, "output staging fits");
@@ -75,11 +83,58 @@ struct RowShared {
   uint8_t pbuf[2 * kPBuf];  // [buffer][head][token] fp32, head rows 144 bytes apart
   int32_t clist[kMaxEntriesPerSplit];
   float xch[2][kRH];  // per token half: the block's per-head maxima or sums, exchanged between halves
+  float smax[kRT / 64];  // per wave: the largest record scale it read when a range is repeated
   int32_t wave_cnt[kRT / 64];
 };
 
 // Position of record r in chunk row c of a tile, and of token r in scale row t.
 __device__ __forceinline__ int rpos(int c, int r) { return r ^ ((c & 1) << 3); }
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// Eight e4m3 codes -> eight fp16 values, exactly (4 exponent and 3 mantissa bits fit fp16's 5 and
+// 10, subnormal codes included).
+__device__ __forceinline__ f16x8 widen8h(uint32_t lo, uint32_t hi) {
+  const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+  const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+  const f16x2 c = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+  const f16x2 d = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+  const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3), cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x16 mfma32_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Largest value over all 64 lanes.
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, m));
+  return x;
+}
+
+// floor(log2(x)) of a positive record scale as a float (0 for 0; the exponent field of x, so
+// 2^-e scales exactly).
+__device__ __forceinline__ float scale_exponent(float x) {
+  const int e = (int)((__float_as_uint(x) >> 23) & 0xffu) - 127;
+  return x > 0.0f ? (float)max(e, -126) : 0.0f;
+}
+
+// The largest record scale of the workgroup's compacted entries, read from the records (all
+// eight waves; only when a range is repeated): this wave's part goes to sh.smax.
+template <typename Shared>
+__device__ __forceinline__ void scan_scales(const DecodeParams& p, const Block& bk, Shared& sh, int w, int tid) {
+  float m = 0.0f;
+  for (int i = tid; i < bk.total; i += kRT) {
+    const f32x4 sc = *reinterpret_cast<const f32x4*>(p.kv + (int64_t)sh.clist[i] * kRecordBytes + kScaleOffset);
+    m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]),
+                                                                       __builtin_elementwise_maximum(sc[2], sc[3])));
+  }
+  m = wave_max64(m);
+  if ((tid & 63) == 0) sh.smax[w] = m;
+}
 
 // Four e4m3 codes -> four bf16 values, exactly.
 __device__ __forceinline__ bf16x4 widen4(uint32_t x) {
@@ -223,6 +278,7 @@ __device__ __forceinline__ Scores score_tile(const uint8_t* tile, const QOps& q,
 
 struct SoftmaxState {
   float m_ref[2], m_raw[2], l_run[2];
+  float shift;  // the power of two folded into m_ref (log2 units)
 };
 
 // Softmax of this lane's scores against each head's reference: probabilities to the heads' rows
@@ -293,8 +349,9 @@ __device__ __forceinline__ void value_tile(const uint8_t* tile, const uint8_t* p
     s1 = *reinterpret_cast<const f32x4*>(srow + x + 4);
   };
   auto pp4 = [](const f32x4& p, const f32x4& s) {
-    return bf16x4{(__bf16)(p[0] * s[0]), (__bf16)(p[1] * s[1]), (__bf16)(p[2] * s[2]), (__bf16)(p[3] * s[3])};
+    return f16x4{(_Float16)(p[0] * s[0]), (_Float16)(p[1] * s[1]), (_Float16)(p[2] * s[2]), (_Float16)(p[3] * s[3])};
   };
+  auto join8h = [](const f16x4& lo, const f16x4& hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); };
 
   f32x4 sv[2][2];
   f32x4 pa[2], pnx[2];
@@ -302,24 +359,24 @@ __device__ __forceinline__ void value_tile(const uint8_t* tile, const uint8_t* p
   sread(0, sv[0][0], sv[0][1]);
   pread(1, pnx[0], pnx[1]);
   sread(1, sv[1][0], sv[1][1]);
-  bf16x8 vt[4];
+  f16x8 vt[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) vt[db] = widen8((uint32_t)cur.raw[0][db][0], (uint32_t)cur.raw[0][db][1]);
-  bf16x8 pp = join8(pp4(pa[0], sv[0][0]), pp4(pa[1], sv[0][1]));
-  bf16x4 nlo, nhi;
+  for (int db = 0; db < 4; ++db) vt[db] = widen8h((uint32_t)cur.raw[0][db][0], (uint32_t)cur.raw[0][db][1]);
+  f16x8 pp = join8h(pp4(pa[0], sv[0][0]), pp4(pa[1], sv[0][1]));
+  f16x4 nlo, nhi;
 #pragma unroll
   for (int ci = 0; ci < 4; ++ci) {
     const int hb = ci & 1, nks = (ci + 1) >> 1;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      O[db][hb] = mfma32_bf16(vt[db], pp, O[db][hb]);
-      if (ci == 1) vt[db] = widen8((uint32_t)cur.raw[1][db][0], (uint32_t)cur.raw[1][db][1]);  // second token half
+      O[db][hb] = mfma32_f16(vt[db], pp, O[db][hb]);
+      if (ci == 1) vt[db] = widen8h((uint32_t)cur.raw[1][db][0], (uint32_t)cur.raw[1][db][1]);  // second token half
       if (ci < 3 && db == 0) nlo = pp4(pnx[0], sv[nks][0]);
       if (ci < 3 && db == 1) {
         nhi = pp4(pnx[1], sv[nks][1]);
         if (ci < 2) pread(ci + 2, pnx[0], pnx[1]);
       }
-      if (ci < 3 && db == 3) pp = join8(nlo, nhi);
+      if (ci < 3 && db == 3) pp = join8h(nlo, nhi);
       if (ci == 2 && db == 0 && next_tile) load_vraw(next_tile, v, lane, nxt);
     }
   }
@@ -385,6 +442,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
   const float cq = p.scale_log2;
   SoftmaxState st;
   st.m_ref[0] = st.m_ref[1] = -INFINITY;
+  st.shift = 0.0f;
   for (int pass = 0; pass < 2; ++pass) {
     st.m_raw[0] = st.m_raw[1] = -INFINITY;
     st.l_run[0] = st.l_run[1] = 0.0f;
@@ -404,9 +462,13 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
           if (G == 0) sh.xch[tb][32 * hh + 16 * hb + r] = mx[hb];
         }
         lds_barrier();  // X
+        // p * scale enters the output MFMAs as fp16: the reference also carries 2^e, e the exponent
+        // of tile 0's largest record scale (found by the value waves), so the products of the first
+        // tile stay below 2^13; the shift cancels in out = O / L and is part of the LSE
+        st.shift = scale_exponent(sh.smax[0]);
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-          st.m_ref[hb] = __builtin_elementwise_maximum(mx[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) * cq;
+          st.m_ref[hb] = __builtin_elementwise_maximum(mx[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) * cq + st.shift;
       }
       if (bk.ntiles > 1) softmax_tile<false>(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
       else softmax_tile<true>(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
@@ -424,16 +486,23 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       mm[hb] = max4x16(st.m_raw[hb] * cq);
-      over = over || mm[hb] > st.m_ref[hb] + kRefHeadroom;
+      over = over || mm[hb] > st.m_ref[hb] - st.shift + kPHeadroom;
     }
-    if (!__syncthreads_or(over)) break;
+    if (!__syncthreads_or(over) || pass == 1) break;  // the value waves vote too: an fp16 product overflowed
+    // the repeat: exact maxima, and the exponent of the largest scale of every record in range,
+    // so that every p * scale * 2^-e is below 2
+    scan_scales(p, bk, sh, s, 64 * s + lane);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
       if (G == 0) sh.xch[tb][32 * hh + 16 * hb + r] = mm[hb];
     __syncthreads();
+    float sm = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kRT / 64; ++k) sm = __builtin_elementwise_maximum(sm, sh.smax[k]);
+    st.shift = scale_exponent(sm);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
-      st.m_ref[hb] = __builtin_elementwise_maximum(mm[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]);
+      st.m_ref[hb] = __builtin_elementwise_maximum(mm[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) + st.shift;
     __syncthreads();  // the exchange slots are free again
   }
   // per-head sums: over the lane groups, then over the two token halves
@@ -495,7 +564,14 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, const Block& b
       }
       VRaw va, vb;  // raw V^T codes of the tile output now (va) and of the next one (vb)
       load_vraw(sh.stage, v, lane, vb);
-      if (pass == 0) lds_barrier();  // X
+      if (pass == 0) {  // tile 0's largest record scale, for the score waves' reference
+        if (v == 0) {
+          const float2 s2 = *reinterpret_cast<const float2*>(sh.stage + kScaleBase + 8 * lane);
+          const float m = wave_max64(__builtin_elementwise_maximum(s2.x, s2.y));
+          if (lane == 0) sh.smax[0] = m;
+        }
+        lds_barrier();  // X
+      }
       for (int n = 1; n < bk.ntiles; ++n) {
         wait_row_tile(n + 1 < bk.ntiles, v);
         lds_barrier();  // Bn: tile n staged; p(n - 1) published; tile n - 2 and p(n - 2) consumed
@@ -513,7 +589,11 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, const Block& b
       value_tile(sh.stage + ((n - 1) % kStages) * kTileBytes, sh.pbuf + ((n - 1) & 1) * kPBuf, vb, O, v, lane, nullptr,
                  va);
     }
-    if (!__syncthreads_or(false)) break;
+    // an fp16 product p * scale that overflowed made every output dim of its head inf or NaN (inf
+    // times a zero code included), so one accumulator per head tells: repeat the range
+    const bool bad = !__builtin_isfinite(O[0][0][0]) || !__builtin_isfinite(O[0][1][0]);
+    if (!__syncthreads_or(bad) || pass == 1) break;
+    scan_scales(p, bk, sh, 4 + v, 256 + 64 * v + lane);
     __syncthreads();
     __syncthreads();
   }

@@ -139,7 +139,8 @@ def test_decode_repeat_is_deterministic():
 def _late_dominant(kv):
     """A row whose head 0 meets, in the 11th 32-entry tile of its list, a record equal to that head's own
     (unscaled) query: its score then exceeds every score of the first tile by ~200 in log2 units, far past the
-    kernel's fixed-reference headroom of 64, so the workgroup redoes its range with the exact max."""
+    kernels' fixed-reference headroom (2^12 for fp8_ds_mla records, 2^64 for bf16 records), so the workgroup
+    redoes its range with the exact max."""
     from workload import pack_records, pack_records_bf16
     w = make_random(321, T=3, H=32, K=400, ctx=600, B=16, n_req=1, kv=kv)
     slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
@@ -169,6 +170,45 @@ def test_decode_late_dominant_score_exceeds_headroom(kv, splits):
                            num_splits=splits, kv_layout=kv)
     torch.cuda.synchronize()
     check_close(out, lse, ro, rl, what=f"late dominant {kv} splits {splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_late_record_scale_overflows_fp16(splits):
+    """The output MFMAs take p * scale in fp16.  Row 1 (query latent set to zero, so every score is a
+    rope product of moderate size) meets, in its 11th tile, a record whose latent values are 2^12 times
+    larger than any of the first tile's and whose rope equals head 0's query rope: its p stays inside
+    the score headroom, but p * scale overflows fp16, the value waves vote to repeat the range, and the
+    repeat scales by the largest record scale of the whole range.  Rows 0 and 2 keep the 2e-2 / 1e-3
+    bars; row 1's values reach ~2^14, so its outputs are held to 2e-3 of their largest magnitude."""
+    from workload import pack_records
+    w = make_random(322, T=3, H=32, K=400, ctx=600, B=16, n_req=1)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    row = 1
+    elsewhere = set(slots[0].tolist()) | set(slots[2].tolist())  # the planted record stays out of rows 0, 2
+    e = next(j for j in range(300, w.K) if slots[row, j] >= 0 and int(slots[row, j]) not in elsewhere)
+    slot = int(slots[row, e])
+    assert int((slots[row, :e] >= 0).sum()) >= 64  # at least two tiles before it
+    q = w.q_f32()
+    q[row, :, :512] = 0.0
+    w.q_bits = torch.from_numpy(np.ascontiguousarray(q)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    i = int(np.searchsorted(w.cache.real_slots, slot))
+    assert w.cache.real_slots[i] == slot
+    lat = np.random.default_rng(5).standard_normal((1, 512)).astype(np.float32) * np.float32(4096.0)
+    w.cache.records[i] = pack_records(lat, q[row, 0, 512:][None, :])[0]
+    ro, rl = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale)
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32,
+                           num_splits=splits)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    big = np.abs(ro[row]).max()
+    assert big > 1000.0  # the planted record carries real weight in row 1
+    print(f"  row 1 max|out| {big:.1f} max|dout| {np.abs(o[row] - ro[row]).max():.3e} "
+          f"max|dlse| {np.abs(l[row] - rl[row]).max():.3e}", flush=True)
+    assert np.abs(o[row] - ro[row]).max() <= 2e-3 * big
+    assert np.abs(l[row] - rl[row]).max() <= 1e-3
+    others = [0, 2]
+    check_close(out[others], lse[others], ro[others], rl[others], what=f"scale overflow rows 0, 2 splits {splits}")
 
 
 @pytest.mark.parametrize("splits", [1, 3])
