@@ -370,11 +370,11 @@ def cpu_baseline(w, budget_s, order=None, what=None, gpu=None):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "2bc7b46a9252eef284f1a8bf19cc0d140bb00e9b44c8c45e56298c0405b8ea9e",
-                  "fetch_bytes": 227163360, "write_bytes": 67420298}
+DECODE_TRAFFIC = {"sources_sha256": "b31f386949e15f5673750b772f6b4508181500183681e180c0d41057eab74b43",
+                  "fetch_bytes": 227191136, "write_bytes": 67426194}
 # SQ counters of the same shard decode (profiles/decode_row_kernel_c3_dcp2_counters.md): MFMA busy =
 # SQ_VALU_MFMA_BUSY_CYCLES per SIMD over busy cycles, LDS busy = SQ_LDS_IDX_ACTIVE per CU over busy cycles
-DECODE_COUNTERS = {"sources_sha256": "2bc7b46a9252eef284f1a8bf19cc0d140bb00e9b44c8c45e56298c0405b8ea9e", "mfma_busy": 0.3207, "lds_busy": 0.2264}
+DECODE_COUNTERS = {"sources_sha256": "b31f386949e15f5673750b772f6b4508181500183681e180c0d41057eab74b43", "mfma_busy": 0.3211, "lds_busy": 0.227}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode_row.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 
