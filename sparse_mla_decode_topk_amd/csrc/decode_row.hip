@@ -147,8 +147,6 @@ __device__ __forceinline__ bf16x8 join8(const bf16x4& lo, const bf16x4& hi) {
 }
 __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) { return join8(widen4(lo), widen4(hi)); }
 
-__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
-
 // One global_load_lds_dwordx4: lane i's 16 bytes from src land at LDS lds + 16 i.  (No immediate
 // offset: on this path it would move the LDS destination as well as the source.)
 __device__ __forceinline__ void dma16(const uint8_t* src, const uint8_t* lds) {
