@@ -116,10 +116,12 @@ __device__ __forceinline__ float wave_max64(float x) {
 }
 
 // floor(log2(x)) of a positive record scale as a float (0 for 0; the exponent field of x, so
-// 2^-e scales exactly).
+// 2^-e scales exactly), at least -100: probabilities carry 2^-e, and with e down to -100 they and
+// their sums stay inside fp32 (scales below 2^-100 only make their products underflow fp16,
+// which at such magnitudes costs nothing measurable).
 __device__ __forceinline__ float scale_exponent(float x) {
   const int e = (int)((__float_as_uint(x) >> 23) & 0xffu) - 127;
-  return x > 0.0f ? (float)max(e, -126) : 0.0f;
+  return x > 0.0f ? (float)max(e, -100) : 0.0f;
 }
 
 // The largest record scale of the workgroup's compacted entries, read from the records (all

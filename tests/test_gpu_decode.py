@@ -211,6 +211,41 @@ def test_decode_late_record_scale_overflows_fp16(splits):
     check_close(out[others], lse[others], ro[others], rl[others], what=f"scale overflow rows 0, 2 splits {splits}")
 
 
+@pytest.mark.parametrize("mode", ["tiny", "huge", "mixed"])
+def test_decode_record_scales_far_from_one(mode):
+    """The fp16 products p * scale are shifted by the exponent of the first tile's largest record
+    scale: record scales multiplied by 2^-60 or 2^60 (every record), or half of the records by 2^30
+    and the rest by 2^-30 (a range fp16 cannot hold at once: the small ones underflow), must give
+    the oracle's result to fp16 precision relative to the row's largest output.  The query's
+    latent part is zero, so the scores (rope only) stay moderate and the LSE keeps the 1e-3 bar."""
+    w = make_random(323, T=4, H=32, K=300, ctx=500, B=16, n_req=2)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    q = w.q_f32()
+    q[:, :, :512] = 0.0
+    w.q_bits = torch.from_numpy(np.ascontiguousarray(q)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rec = w.cache.records
+    sc = rec[:, 512:528].copy().view("<f4")  # [n, 4] record scales
+    n = rec.shape[0]
+    if mode == "tiny":
+        f = np.full(n, 2.0 ** -60, np.float32)
+    elif mode == "huge":
+        f = np.full(n, 2.0 ** 60, np.float32)
+    else:
+        f = np.where(np.arange(n) % 2 == 0, np.float32(2.0 ** 30), np.float32(2.0 ** -30))
+    rec[:, 512:528] = (sc * f[:, None]).astype("<f4").view(np.uint8)  # powers of two: exact
+    ro, rl = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale)
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    for t in range(w.T):
+        big = np.abs(ro[t]).max()
+        d = np.abs(o[t] - ro[t]).max()
+        print(f"  {mode} row {t}: max|out| {big:.3e} max|dout|/max|out| {d / big:.2e}", flush=True)
+        assert d <= 2e-3 * big
+    assert np.abs(l - rl).max() <= 1e-3
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_decode_query_ranges_per_head(splits):
     """Heads of q scaled by powers of two from 2^-110 to 2^3, and one all-zero head: q enters the
