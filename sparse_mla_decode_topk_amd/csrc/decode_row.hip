@@ -83,7 +83,7 @@ struct RowShared {
   uint8_t pbuf[2 * kPBuf];  // [buffer][head][token] fp32, head rows 144 bytes apart
   int32_t clist[kMaxEntriesPerSplit];
   float xch[2][kRH];  // per token half: the block's per-head maxima or sums, exchanged between halves
-  float smax[kRT / 64];  // per wave: the largest record scale it read when a range is repeated
+  float smax[kRT / 64];  // largest record scales: tile 0's in [0] (first pass), per wave when a range is repeated
   int32_t wave_cnt[kRT / 64];
 };
 
@@ -480,7 +480,8 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
       }
       lds_barrier();  // Blast
     }
-    // a second pass, with the exact max as reference, only if some score outgrew the headroom
+    // a second pass, with the exact max as reference, only if some score outgrew the headroom or
+    // (the value waves' vote) some fp16 product p * scale overflowed
     float mm[2];
     bool over = false;
 #pragma unroll
