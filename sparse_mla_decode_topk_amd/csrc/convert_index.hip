@@ -7,9 +7,12 @@
 // FlashInfer sparse MLA", "Summary": the per-row valid counts are produced alongside.
 //
 // One workgroup per row; consecutive lanes take consecutive entries (coalesced int32
-// traffic).  Each thread handles kPer entries per pass with all of their id loads in flight
+// traffic).  Each thread handles PER entries per pass with all of their id loads in flight
 // together, then all of their block-table loads, so a row costs two dependent memory round
-// trips instead of two per entry.  Power-of-two block size, DCP size and interleave (the
+// trips instead of two per entry.  A batch of up to 1024 rows runs 1024 threads per row (two
+// entries each for top-k 2048: the few workgroups then keep more loads in flight per CU); a
+// larger one runs 256 (eight each), which measured faster once the rows fill the GPU several
+// times over.  Power-of-two block size, DCP size and interleave (the
 // usual case) take shifts and masks instead of integer division.  The row's valid count is
 // a workgroup reduction, so no atomics and no pre-zeroed output are needed.
 
@@ -18,15 +21,13 @@
 namespace smla {
 namespace {
 
-constexpr int kConvThreads = 256;
-constexpr int kPer = 8;  // entries per thread per pass
-
 // x / d and x % d for x >= 0, d >= 1; `lg` is log2(d) when d is a power of two, else -1.
 __device__ __forceinline__ int div_pos(int x, int d, int lg) { return lg >= 0 ? x >> lg : x / d; }
 __device__ __forceinline__ int mod_pos(int x, int d, int lg) { return lg >= 0 ? x & (d - 1) : x % d; }
 
-__global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) {
-  __shared__ int wsum[kConvThreads / 64];
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void convert_kernel(ConvertParams p) {
+  __shared__ int wsum[NT / 64];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t* ids = p.ids + (int64_t)t * p.ids_ld;
@@ -36,16 +37,16 @@ __global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) 
   const int32_t* btrow = p.bt + (int64_t)(req_ok ? b : 0) * p.bt_ld;
   const int D = p.dcp_size, I = p.interleave, r = p.dcp_rank, B = p.block_size;
   int count = 0;
-  for (int base = 0; base < p.K; base += kConvThreads * kPer) {
-    int id[kPer];
+  for (int base = 0; base < p.K; base += NT * PER) {
+    int id[PER];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int j = base + i * kConvThreads + tid;
+    for (int i = 0; i < PER; ++i) {
+      const int j = base + i * NT + tid;
       id[i] = j < p.K ? ids[j] : -1;
     }
-    int blk[kPer], off[kPer];  // block-table column and offset in the block; blk = -1: no slot
+    int blk[PER], off[PER];  // block-table column and offset in the block; blk = -1: no slot
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < PER; ++i) {
       blk[i] = -1;
       off[i] = 0;
       const int x = id[i];
@@ -64,12 +65,12 @@ __global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) 
         }
       }
     }
-    int phys[kPer];
+    int phys[PER];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) phys[i] = blk[i] >= 0 ? btrow[blk[i]] : -1;
+    for (int i = 0; i < PER; ++i) phys[i] = blk[i] >= 0 ? btrow[blk[i]] : -1;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int j = base + i * kConvThreads + tid;
+    for (int i = 0; i < PER; ++i) {
+      const int j = base + i * NT + tid;
       int slot = -1;
       if (phys[i] >= 0) {
         const int64_t s = (int64_t)phys[i] * B + off[i];
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kConvThreads) void convert_kernel(ConvertParams p) 
   if (tid == 0) {
     int s = 0;
 #pragma unroll
-    for (int w = 0; w < kConvThreads / 64; ++w) s += wsum[w];
+    for (int w = 0; w < NT / 64; ++w) s += wsum[w];
     p.valid[t] = s;
   }
 }
@@ -106,7 +107,10 @@ hipError_t launch_convert(const ConvertParams& p_in, hipStream_t stream) {
   p.lg_block = log2_exact(p.block_size);
   p.lg_dcp = log2_exact(p.dcp_size);
   p.lg_interleave = log2_exact(p.interleave);
-  hipLaunchKernelGGL(convert_kernel, dim3(p.T), dim3(kConvThreads), 0, stream, p);
+  if (p.T <= 1024)
+    hipLaunchKernelGGL((convert_kernel<1024, 2>), dim3(p.T), dim3(1024), 0, stream, p);
+  else
+    hipLaunchKernelGGL((convert_kernel<256, 8>), dim3(p.T), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
