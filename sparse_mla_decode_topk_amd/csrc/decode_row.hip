@@ -138,6 +138,16 @@ __device__ __forceinline__ void scan_scales(const DecodeParams& p, const Block& 
   if ((tid & 63) == 0) sh.smax[w] = m;
 }
 
+// e of a repeated range: the exponent of the largest record scale that scan_scales found (at
+// most 126, so that 2^-e and 2^e are normal floats).
+template <typename Shared>
+__device__ __forceinline__ int repeat_exponent(const Shared& sh) {
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kRT / 64; ++k) m = __builtin_elementwise_maximum(m, sh.smax[k]);
+  return min((int)scale_exponent(m), 126);
+}
+
 // Four e4m3 codes -> four bf16 values, exactly.
 __device__ __forceinline__ bf16x4 widen4(uint32_t x) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
@@ -278,15 +288,29 @@ __device__ __forceinline__ Scores score_tile(const uint8_t* tile, const QOps& q,
 
 struct SoftmaxState {
   float m_ref[2], m_raw[2], l_run[2];
-  float shift;  // the power of two folded into m_ref (log2 units)
+  float shift[2];  // the power of two folded into m_ref (log2 units)
 };
+
+// A reference below this magnitude (log2 units) takes the integer shift exactly; a larger one is
+// left unshifted (its products are checked like any other).
+constexpr float kExactFold = 1048576.0f;
 
 // Softmax of this lane's scores against each head's reference: probabilities to the heads' rows
 // of `pn`, running raw max and sum.  kMask: entries at or past `nin` get p = 0 (only a range's
-// last tile can hold such entries; the other tiles skip the compare and select).
-template <bool kMask>
+// last tile can hold such entries; the other tiles skip the compare and select).  kExact: the
+// reference is the largest rounded product score * cq, and each exponent is that rounded product
+// minus the reference, so none exceeds 0 (a fused score * cq - ref exceeds 0 by up to half an ulp
+// of the reference: more than 1 once references pass 2^25, an fp32 overflow of p past 2^31), and
+// the probabilities handed to the value waves carry c = 2^-e (the sums do not).
+// x * c rounded to fp32, then minus m (two roundings: never fused into one fma).
+__device__ __forceinline__ float rounded_product_minus(float x, float c, float m) {
+#pragma clang fp contract(off)
+  return x * c - m;
+}
+
+template <bool kMask, bool kExact>
 __device__ __forceinline__ void softmax_tile(const Scores& S, int tb, int hh, int G, int r, int nin, float cq,
-                                             SoftmaxState& st, uint8_t* pn) {
+                                             SoftmaxState& st, uint8_t* pn, float c) {
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     f32x4 t;
@@ -294,9 +318,10 @@ __device__ __forceinline__ void softmax_tile(const Scores& S, int tb, int hh, in
     for (int i = 0; i < 4; ++i) {
       const float v = !kMask || 16 * tb + 4 * G + i < nin ? S.s[hb][i] : -INFINITY;
       st.m_raw[hb] = __builtin_elementwise_maximum(st.m_raw[hb], v);
-      t[i] = fast_exp2(fmaf(v, cq, -st.m_ref[hb]));
+      t[i] = fast_exp2(kExact ? rounded_product_minus(v, cq, st.m_ref[hb]) : fmaf(v, cq, -st.m_ref[hb]));
       st.l_run[hb] += t[i];
     }
+    if (kExact) t *= c;
     const int row = 32 * hh + 16 * hb + r;
     *reinterpret_cast<f32x4*>(pn + row * kPRow + 16 * (4 * tb + G)) = t;
   }
@@ -435,6 +460,51 @@ __device__ __forceinline__ void store_staged(const DecodeParams& p, const Block&
 //   per pass: the "over" vote; after a vote for a second pass: two exchange barriers.
 //   Then E (sums published) and the output staging rounds.
 
+// One pass of a score wave over the range: scores, softmax and probabilities of every tile.
+// kRepeat: a repeated range, whose references are the exact maxima and whose probabilities go to
+// the value waves times c.
+template <bool kRepeat>
+__device__ __forceinline__ void score_pass(const Block& bk, RowShared& sh, const QOps& q, int tb, int hh, int G, int r,
+                                           float cq, SoftmaxState& st, float c) {
+  if (bk.ntiles == 0) return;
+  lds_barrier();  // B0
+  const Scores S = score_tile(sh.stage, q, tb, G, r);
+  const int nin = min(kTT, bk.total);
+  if (!kRepeat) {  // reference: the max of each head over tile 0, from both token halves
+    float mx[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      mx[hb] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mx[hb] = __builtin_elementwise_maximum(mx[hb], 16 * tb + 4 * G + i < nin ? S.s[hb][i] : -INFINITY);
+      mx[hb] = max4x16(mx[hb]);
+      if (G == 0) sh.xch[tb][32 * hh + 16 * hb + r] = mx[hb];
+    }
+    lds_barrier();  // X
+    // p * scale enters the output MFMAs as fp16: the reference also carries 2^e, e the exponent
+    // of tile 0's largest record scale (found by the value waves), so the products of the first
+    // tile stay below 2^13; the shift cancels in out = O / L and is part of the LSE.  A reference
+    // too large to take the integer e exactly keeps e = 0.
+    const float e = scale_exponent(sh.smax[0]);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float m = __builtin_elementwise_maximum(mx[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) * cq;
+      st.shift[hb] = __builtin_fabsf(m) < kExactFold ? e : 0.0f;
+      st.m_ref[hb] = m + st.shift[hb];
+    }
+  }
+  if (bk.ntiles > 1) softmax_tile<false, kRepeat>(S, tb, hh, G, r, nin, cq, st, sh.pbuf, c);
+  else softmax_tile<true, kRepeat>(S, tb, hh, G, r, nin, cq, st, sh.pbuf, c);
+  for (int n = 1; n < bk.ntiles; ++n) {
+    lds_barrier();  // Bn
+    const Scores Sn = score_tile(sh.stage + (n % kStages) * kTileBytes, q, tb, G, r);
+    if (n + 1 < bk.ntiles) softmax_tile<false, kRepeat>(Sn, tb, hh, G, r, kTT, cq, st, sh.pbuf + (n & 1) * kPBuf, c);
+    else softmax_tile<true, kRepeat>(Sn, tb, hh, G, r, bk.total - n * kTT, cq, st, sh.pbuf + (n & 1) * kPBuf, c);
+  }
+  lds_barrier();  // Blast
+}
+
 __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& bk, RowShared& sh, int s, int lane,
                                            const QOps& q) {
   const int G = lane >> 4, r = lane & 15;
@@ -442,44 +512,13 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
   const float cq = p.scale_log2;
   SoftmaxState st;
   st.m_ref[0] = st.m_ref[1] = -INFINITY;
-  st.shift = 0.0f;
+  st.shift[0] = st.shift[1] = 0.0f;
+  float c = 1.0f;  // a repeated range: 2^-e on the probabilities of the output MFMAs
   for (int pass = 0; pass < 2; ++pass) {
     st.m_raw[0] = st.m_raw[1] = -INFINITY;
     st.l_run[0] = st.l_run[1] = 0.0f;
-    if (bk.ntiles > 0) {
-      lds_barrier();  // B0
-      const Scores S = score_tile(sh.stage, q, tb, G, r);
-      const int nin = min(kTT, bk.total);
-      if (pass == 0) {  // reference: the max of each head over tile 0, from both token halves
-        float mx[2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          mx[hb] = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            mx[hb] = __builtin_elementwise_maximum(mx[hb], 16 * tb + 4 * G + i < nin ? S.s[hb][i] : -INFINITY);
-          mx[hb] = max4x16(mx[hb]);
-          if (G == 0) sh.xch[tb][32 * hh + 16 * hb + r] = mx[hb];
-        }
-        lds_barrier();  // X
-        // p * scale enters the output MFMAs as fp16: the reference also carries 2^e, e the exponent
-        // of tile 0's largest record scale (found by the value waves), so the products of the first
-        // tile stay below 2^13; the shift cancels in out = O / L and is part of the LSE
-        st.shift = scale_exponent(sh.smax[0]);
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          st.m_ref[hb] = __builtin_elementwise_maximum(mx[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) * cq + st.shift;
-      }
-      if (bk.ntiles > 1) softmax_tile<false>(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
-      else softmax_tile<true>(S, tb, hh, G, r, nin, cq, st, sh.pbuf);
-      for (int n = 1; n < bk.ntiles; ++n) {
-        lds_barrier();  // Bn
-        const Scores Sn = score_tile(sh.stage + (n % kStages) * kTileBytes, q, tb, G, r);
-        if (n + 1 < bk.ntiles) softmax_tile<false>(Sn, tb, hh, G, r, kTT, cq, st, sh.pbuf + (n & 1) * kPBuf);
-        else softmax_tile<true>(Sn, tb, hh, G, r, bk.total - n * kTT, cq, st, sh.pbuf + (n & 1) * kPBuf);
-      }
-      lds_barrier();  // Blast
-    }
+    if (pass == 0) score_pass<false>(bk, sh, q, tb, hh, G, r, cq, st, 1.0f);
+    else score_pass<true>(bk, sh, q, tb, hh, G, r, cq, st, c);
     // a second pass, with the exact max as reference, only if some score outgrew the headroom or
     // (the value waves' vote) some fp16 product p * scale overflowed
     float mm[2];
@@ -487,23 +526,24 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       mm[hb] = max4x16(st.m_raw[hb] * cq);
-      over = over || mm[hb] > st.m_ref[hb] - st.shift + kPHeadroom;
+      over = over || mm[hb] > st.m_ref[hb] - st.shift[hb] + kPHeadroom;
     }
     if (!__syncthreads_or(over) || pass == 1) break;  // the value waves vote too: an fp16 product overflowed
-    // the repeat: exact maxima, and the exponent of the largest scale of every record in range,
-    // so that every p * scale * 2^-e is below 2
+    // the repeat: exact maxima as references (p <= 1), and the probabilities of the output MFMAs
+    // times 2^-e, e the exponent of the largest scale of every record in range (scan_scales), so
+    // that every fp16 product is below 2 however large the references are; the value waves
+    // multiply their output by 2^e
     scan_scales(p, bk, sh, s, 64 * s + lane);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
       if (G == 0) sh.xch[tb][32 * hh + 16 * hb + r] = mm[hb];
     __syncthreads();
-    float sm = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kRT / 64; ++k) sm = __builtin_elementwise_maximum(sm, sh.smax[k]);
-    st.shift = scale_exponent(sm);
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-      st.m_ref[hb] = __builtin_elementwise_maximum(mm[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]) + st.shift;
+    for (int hb = 0; hb < 2; ++hb) {
+      st.m_ref[hb] = __builtin_elementwise_maximum(mm[hb], sh.xch[tb ^ 1][32 * hh + 16 * hb + r]);
+      st.shift[hb] = 0.0f;
+    }
+    c = ldexpf(1.0f, -repeat_exponent(sh));
     __syncthreads();  // the exchange slots are free again
   }
   // per-head sums: over the lane groups, then over the two token halves
@@ -547,6 +587,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, const Block& b
 
 __device__ __forceinline__ void value_role(const DecodeParams& p, const Block& bk, RowShared& sh, int v, int lane) {
   f32x16 O[4][2];
+  float up = 1.0f;  // 2^e: a repeated range's probabilities carry 2^-e, given back to the output here
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -596,6 +637,7 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, const Block& b
     if (!__syncthreads_or(bad) || pass == 1) break;
     scan_scales(p, bk, sh, 4 + v, 256 + 64 * v + lane);
     __syncthreads();
+    up = ldexpf(1.0f, repeat_exponent(sh));
     __syncthreads();
   }
   __syncthreads();  // E: the per-head sums are in sh.xch
@@ -606,7 +648,7 @@ __device__ __forceinline__ void value_role(const DecodeParams& p, const Block& b
   for (int hb = 0; hb < 2; ++hb) {
     const int hl = 32 * hb + r32;
     const float lt = sh.xch[0][hl] + sh.xch[1][hl];
-    inv[hb] = p.splits > 1 ? 1.0f : (lt > 0.0f ? 1.0f / lt : 0.0f);
+    inv[hb] = p.splits > 1 ? up : (lt > 0.0f ? up / lt : 0.0f);
   }
   const int tid = 256 + 64 * v + lane;
   if (p.splits > 1 || p.out_fp32) {

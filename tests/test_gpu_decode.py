@@ -246,6 +246,45 @@ def test_decode_record_scales_far_from_one(mode):
     assert np.abs(l - rl).max() <= 1e-3
 
 
+@pytest.mark.parametrize("seed,T,H,K,ctx,B,n_req,neg,splits,k", [
+    (10195, 5, 128, 537, 221, 16, 2, 0.0, 0, 25),
+    (10133, 6, 16, 1071, 1564, 64, 3, 0.0, 5, 26),
+    (10092, 2, 96, 1826, 2089, 64, 1, 0.5, 3, 29),
+])
+def test_decode_logits_past_fp32_resolution(seed, T, H, K, ctx, B, n_req, neg, splits, k):
+    """Every record scale multiplied by 2^k with the query kept whole: the scores reach 2^28 .. 2^33
+    in log2 units, where an fp32 score is a multiple of 16 .. 512 and the weights are close to one-hot.
+    A fused score * cq - ref may then exceed 0 by half an ulp of the reference (p up to 2^256); the
+    repeated range rounds the product first, so every p <= 1 and the output stays finite and, the
+    largest scores being well apart here, matches the oracle to fp16 precision relative to each row's
+    largest output.  The LSE is held to the relative precision of the fp32 scores it comes from
+    (1e-6 of |lse|, i.e. about 16 units of fp32 rounding)."""
+    w = make_random(seed, T=T, H=H, K=K, ctx=ctx, B=B, neg_frac=neg, n_req=n_req)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    rec = w.cache.records
+    sc = rec[:, 512:528].copy().view("<f4")
+    rec[:, 512:528] = (sc * np.float32(2.0 ** k)).astype("<f4").view(np.uint8)  # a power of two: exact
+    ro, rl = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale)
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32,
+                           num_splits=splits)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(l), fin) and np.all(o[~fin] == 0.0)
+    assert np.abs(rl[fin]).max() > 1e8
+    for t in range(w.T):
+        if not fin[t].any():
+            continue
+        big = np.abs(ro[t]).max()
+        d = np.abs(o[t] - ro[t]).max()
+        print(f"  2^{k} row {t}: max|out| {big:.3e} max|dout|/max|out| {d / big:.2e}", flush=True)
+        assert d <= 2e-3 * big
+    dl = np.abs(l[fin] - rl[fin])
+    print(f"  2^{k}: max|lse| {np.abs(rl[fin]).max():.3e} max|dlse|/|lse| {(dl / np.abs(rl[fin])).max():.2e}", flush=True)
+    assert np.all(dl <= 1e-6 * np.abs(rl[fin]) + 1e-3)
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_decode_query_ranges_per_head(splits):
     """Heads of q scaled by powers of two from 2^-110 to 2^3, and one all-zero head: q enters the
