@@ -104,6 +104,15 @@ __device__ __forceinline__ const uint8_t* lane_record(const DecodeParams& p, con
   return p.kv + (int64_t)sh.clist[idx] * kRecB + 16 * (lane >> 4);
 }
 
+// Largest per-lane sum of a pass whose probabilities all stay within the headroom: 2^64 each,
+// at most 2^8 tokens per lane (4096 entries over 16 lanes).
+constexpr float kMaxLaneSum = 0x1p72f;
+
+template <bool B>
+struct PassTag {
+  static constexpr bool value = B;
+};
+
 // ---------------------------------------------------------------------------------------
 // Score wave `sw` (0..3): heads h_lo + 16sw + 0..15.  Query operand: lane holds head
 // 16sw + (lane & 15) and dims 32ks + 8g .. +7 of every k-step ks (g = lane >> 4).  Scores
@@ -135,7 +144,12 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
     m_raw[r] = -INFINITY;
     l_run[r] = 0.0f;
   }
-  for (int pass = 0; pass < 2; ++pass) {
+  // The tile loop of one pass.  The first pass takes each head's max over the first tile as its
+  // reference; a repeated range (kExact) takes the exact max, and rounds each product score * cq
+  // before subtracting it, so that no exponent exceeds 0 (a fused product and difference exceeds
+  // 0 by up to half an ulp of the reference, which overflows p once references pass 2^31).
+  auto tiles = [&](auto exact) {
+    constexpr bool kExact = decltype(exact)::value;
     for (int n = 0; n <= bk.ntiles; ++n) {
       lds_barrier();  // tile n staged; P(n-2) consumed by the value waves
       if (!active || n >= bk.ntiles) continue;
@@ -156,7 +170,7 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) m_raw[r] = __builtin_elementwise_maximum(m_raw[r], pv[r]);
-      if (pass == 0 && n == 0) {
+      if (!kExact && n == 0) {
         // the reference of the first pass: each head's max over the first tile (scaling by
         // cq > 0 commutes with the max)
 #pragma unroll
@@ -164,20 +178,26 @@ __device__ __forceinline__ void score_role(const DecodeParams& p, Shared& sh, co
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = fast_exp2(fmaf(pv[r], cq, -m_ref[r]));
+        pv[r] = fast_exp2(kExact ? rounded_product_minus(pv[r], cq, m_ref[r]) : fmaf(pv[r], cq, -m_ref[r]));
         l_run[r] += pv[r];
       }
       // P = bf16(p) as [token][head]: this lane's heads 16sw + 4g .. +3 of token tok
       *reinterpret_cast<bf16x4*>(sh.pbuf + (n & 1) * kPTile + tok * kPRow + 8 * pseg) =
           bf16x4{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
     }
-    // a second pass, with the exact max as reference, only if some score outgrew the headroom
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 0) tiles(PassTag<false>{});
+    else tiles(PassTag<true>{});
+    // a second pass, with the exact max as reference, only if some score outgrew the headroom or
+    // some probability overflowed (a score of the first tile may exceed its own rounded product,
+    // the reference, by half an ulp: past 2^31 that alone is more than 2^128)
     bool over = false;
     float m_max[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       m_max[r] = active ? max16(m_raw[r]) * cq : -INFINITY;
-      over |= m_max[r] > m_ref[r] + kRefHeadroom;
+      over |= m_max[r] > m_ref[r] + kRefHeadroom || !(l_run[r] <= kMaxLaneSum);
     }
     if (!__syncthreads_or(over)) break;
 #pragma unroll

@@ -32,6 +32,14 @@ constexpr int kHB = kHeadsPerBlock;    // 64 heads per workgroup
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x * c rounded to fp32, then minus m (two roundings: never fused into one fma).  A repeated
+// range's exponents take this form against the largest rounded product, so none exceeds 0; a
+// fused x * c - m exceeds 0 by up to half an ulp of m.
+__device__ __forceinline__ float rounded_product_minus(float x, float c, float m) {
+#pragma clang fp contract(off)
+  return x * c - m;
+}
+
 __device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

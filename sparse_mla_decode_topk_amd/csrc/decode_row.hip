@@ -302,12 +302,6 @@ constexpr float kExactFold = 1048576.0f;
 // minus the reference, so none exceeds 0 (a fused score * cq - ref exceeds 0 by up to half an ulp
 // of the reference: more than 1 once references pass 2^25, an fp32 overflow of p past 2^31), and
 // the probabilities handed to the value waves carry c = 2^-e (the sums do not).
-// x * c rounded to fp32, then minus m (two roundings: never fused into one fma).
-__device__ __forceinline__ float rounded_product_minus(float x, float c, float m) {
-#pragma clang fp contract(off)
-  return x * c - m;
-}
-
 template <bool kMask, bool kExact>
 __device__ __forceinline__ void softmax_tile(const Scores& S, int tb, int hh, int G, int r, int nin, float cq,
                                              SoftmaxState& st, uint8_t* pn, float c) {

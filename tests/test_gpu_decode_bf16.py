@@ -95,3 +95,34 @@ def test_bf16_long_context_h128_sampled():
     ro, rl = O.attention_rows(sub.q_f32(), slots[rows], w.cache, w.cache.num_slots, w.sm_scale, record_layout="bf16")
     check_close(out[rows], lse[rows], ro, rl, what="bf16 H128 K2048")
     assert not torch.isnan(out).any() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("k", [24, 40])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_bf16_logits_past_fp32_resolution(k, splits):
+    """q multiplied by 2^k (exact in bf16): the scores reach about 2^(k + 4) in log2 units, where a
+    fused score * cq - ref exceeds 0 by up to half an ulp of the reference (p = inf once that passes
+    2^7).  The first pass sends an overflowed sum to the repeat, which rounds each product before
+    subtracting the exact max, so every p <= 1; the weights are then one-hot to fp32 precision and the
+    output matches the oracle's to 2e-3 of each row's largest output.  The LSE is held to 1e-6 of
+    |lse| (the relative precision of the fp32 scores it comes from)."""
+    w = make_random(4100 + k, T=6, H=64, K=500, ctx=900, B=32, neg_frac=0.1, n_req=2, kv="bf16")
+    q = w.q_f32() * np.float32(2.0 ** k)
+    w.q_bits = torch.from_numpy(np.ascontiguousarray(q)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32,
+                           kv_layout="bf16", num_splits=splits)
+    torch.cuda.synchronize()
+    ro, rl = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale, record_layout="bf16")
+    o, l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(l), fin) and np.abs(rl[fin]).max() > 2.0 ** k
+    for t in range(w.T):
+        big = np.abs(ro[t]).max()
+        d = np.abs(o[t] - ro[t]).max()
+        print(f"  2^{k} splits {splits} row {t}: max|out| {big:.3e} max|dout|/max|out| {d / big:.2e}", flush=True)
+        assert d <= 2e-3 * big
+    dl = np.abs(l[fin] - rl[fin])
+    print(f"  2^{k}: max|lse| {np.abs(rl[fin]).max():.3e} max|dlse|/|lse| {(dl / np.abs(rl[fin])).max():.2e}", flush=True)
+    assert np.all(dl <= 1e-6 * np.abs(rl[fin]) + 1e-3)
