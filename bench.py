@@ -370,11 +370,11 @@ def cpu_baseline(w, budget_s, order=None, what=None, gpu=None):
 # HBM bytes per decode launch of this workload, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, each with --copy-mib 1024) scaled by what the same counters
 # read for the plain 1 GiB device copy.  Valid only for the kernel sources they were taken on.
-DECODE_TRAFFIC = {"sources_sha256": "53d3006c881aaa4ad5bf6325bf4d3cacd73fedb6dbe45ddb6ab6619c9e209e29",
+DECODE_TRAFFIC = {"sources_sha256": "14d748d1ae38070c495fe5edfc7a180e8697f0f030d074df6bfd849eee8079b0",
                   "fetch_bytes": 227193197, "write_bytes": 67428577}
 # SQ counters of the same shard decode (profiles/decode_row_kernel_c3_dcp2_counters.md): MFMA busy =
 # SQ_VALU_MFMA_BUSY_CYCLES per SIMD over busy cycles, LDS busy = SQ_LDS_IDX_ACTIVE per CU over busy cycles
-DECODE_COUNTERS = {"sources_sha256": "53d3006c881aaa4ad5bf6325bf4d3cacd73fedb6dbe45ddb6ab6619c9e209e29", "mfma_busy": 0.3203, "lds_busy": 0.2265}
+DECODE_COUNTERS = {"sources_sha256": "14d748d1ae38070c495fe5edfc7a180e8697f0f030d074df6bfd849eee8079b0", "mfma_busy": 0.3203, "lds_busy": 0.2265}
 KERNEL_SOURCES = ("sparse_mla_decode_topk_amd/csrc/decode_row.hip", "sparse_mla_decode_topk_amd/csrc/decode_common.h",
                   "sparse_mla_decode_topk_amd/csrc/smla_internal.h")
 

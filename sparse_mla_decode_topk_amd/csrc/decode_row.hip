@@ -297,7 +297,7 @@ constexpr float kExactFold = 1048576.0f;
 
 // Softmax of this lane's scores against each head's reference: probabilities to the heads' rows
 // of `pn`, running raw max and sum.  kMask: entries at or past `nin` get p = 0 (only a range's
-// last tile can hold such entries; the other tiles skip the compare and select).  kExact: the
+// last tile can hold such entries).  kExact: the
 // reference is the largest rounded product score * cq, and each exponent is that rounded product
 // minus the reference, so none exceeds 0 (a fused score * cq - ref exceeds 0 by up to half an ulp
 // of the reference: more than 1 once references pass 2^25, an fp32 overflow of p past 2^31), and
