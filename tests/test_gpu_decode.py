@@ -387,3 +387,60 @@ def test_decode_valid_count_matches_slots(kv, H, splits):
     assert torch.all(o[7] == 0) and torch.all(torch.isneginf(l[7]))
     keep = [t for t in range(w.T) if t != 7]
     assert torch.equal(l[keep], a[1][keep])
+
+
+@pytest.mark.parametrize("case", range(48))
+def test_decode_random_sweep(case):
+    """Seeded random combinations: T 1-8, H a multiple of 16 up to 128, K 1-3000 over contexts of
+    40-3000 tokens, -1 shares 0-0.9, 1-5 forced splits or the automatic plan, block sizes 16/64,
+    and one of: plain records, every record scale times its own power of two in [2^-20, 2^20], all
+    scales times one power of two in [2^-30, 2^30], 2 % of the records 2^8 larger; a quarter of
+    the cases zero the query's latent part.  Bars: the 2e-2 / 1e-3 of the other tests; where the
+    scales are rescaled, out within 2e-3 of the largest output when that is larger (fp16 products,
+    as in test_decode_record_scales_far_from_one), and the LSE within 1e-6 of its magnitude when
+    the rescaled scores pass 1000 (the precision of the fp32 scores it comes from)."""
+    rng = np.random.default_rng(7000 + case)
+    T = int(rng.integers(1, 9))
+    H = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    ctx = int(rng.integers(40, 3001))
+    K = int(rng.integers(1, 3001))
+    neg = float(rng.choice([0.0, 0.1, 0.5, 0.9]))
+    splits = int(rng.choice([0, 1, 2, 3, 5]))
+    mode = int(rng.integers(0, 4))
+    zero_lat = bool(rng.integers(0, 4) == 0)
+    B = int(rng.choice([16, 64]))
+    n_req = int(rng.integers(1, T + 1))
+    w = make_random(8000 + case, T=T, H=H, K=K, ctx=ctx, B=B, neg_frac=neg, n_req=n_req)
+    slots, _ = O.convert_index(w.ids, w.req, w.block_table, w.block_size)
+    if mode:
+        rec = w.cache.records
+        sc = rec[:, 512:528].copy().view("<f4")
+        n = rec.shape[0]
+        if mode == 1:
+            f = np.float32(2.0) ** rng.integers(-20, 21, size=n).astype(np.float32)
+        elif mode == 2:
+            f = np.full(n, np.float32(2.0) ** int(rng.integers(-30, 31)), np.float32)
+        else:
+            f = np.where(rng.random(n) < 0.02, np.float32(256.0), np.float32(1.0))
+        rec[:, 512:528] = (sc * f[:, None]).astype("<f4").view(np.uint8)  # powers of two: exact
+    if zero_lat:
+        q = w.q_f32()
+        q[:, :, :512] = 0.0
+        w.q_bits = torch.from_numpy(np.ascontiguousarray(q)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    print(f"sweep {case}: T={T} H={H} K={K} ctx={ctx} neg={neg} splits={splits} mode={mode} zero_lat={zero_lat}",
+          flush=True)
+    ro, rl = O.attention_rows(w.q_f32(), slots, w.cache, w.cache.num_slots, w.sm_scale)
+    out, lse = smla.decode(q_dev(w), w.cache.to_device("cuda"), dev(slots), w.sm_scale, out_dtype=torch.float32,
+                           num_splits=splits)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert not np.isnan(o).any() and not np.isnan(l).any()
+    assert np.array_equal(np.isneginf(l), np.isneginf(rl)) and np.all(o[np.isneginf(rl)] == 0.0)
+    fin = np.isfinite(rl)
+    big = float(np.max(np.abs(ro), initial=0.0))
+    tol = max(2e-2, 2e-3 * big) if mode else 2e-2
+    ltol = 1e-3 * max(1.0, float(np.max(np.abs(rl[fin]), initial=1.0)) / 1000.0) if (mode and not zero_lat) else 1e-3
+    do = float(np.max(np.abs(o - ro), initial=0.0))
+    dl = float(np.max(np.abs(l[fin] - rl[fin]), initial=0.0))
+    print(f"  max|dout| {do:.3e} (bar {tol:.2e})  max|dlse| {dl:.3e} (bar {ltol:.1e})", flush=True)
+    assert do <= tol and dl <= ltol
